@@ -1,0 +1,202 @@
+/*
+ * msgl.h — C ABI of the paged-KV attention library (gfx950 / MI355X).
+ *
+ * Operations (all from the mini-sglang pages):
+ *   msgl_store_kv      scatter new K/V rows into the pool at out_loc
+ *                      ["Mini-SGLang complete analysis", §4.4.3 (pool tensor,
+ *                      flattened per layer to (slots, kv heads, head_dim)),
+ *                      §4.6.7 (the attention layer stores first), §4.9.4 (the
+ *                      store kernel's shape contract), §4.9.5 (vector copies)]
+ *   msgl_paged_decode  one query token per request, GQA, keys gathered through
+ *                      a token-granular page-table row
+ *                      [same page, §1.2 (decode is memory-bound), §1.4 (paged
+ *                      pool + per-request page table), §4.5.3 (GQA ratio),
+ *                      §4.6.4 (table kept at page_size 1)]
+ *   msgl_paged_extend  causal chunked-prefill attention over a cached prefix
+ *                      plus the chunk itself
+ *                      ["Deep dive into mini-sglang: chunked prefill and
+ *                      overlap scheduling", chunked-prefill section;
+ *                      "Mini-SGLang complete analysis" §4.2.3 (cached_len /
+ *                      extend_len), §4.6.5 (cu_seqlens_q)]
+ *   msgl_merge_states  log-sum-exp merge of partial attention results (the
+ *                      pages do not describe split-KV; the merge is the exact
+ *                      identity that recombines a softmax split over disjoint
+ *                      key sets)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensor arguments are DEVICE pointers owned by the caller.  The library
+ *   never allocates, frees or synchronises; every call only enqueues work on
+ *   `stream` and returns.  Buffers must stay alive and unmodified until that
+ *   work has completed (the pages' rule against freeing a batch's inputs while
+ *   the GPU may still read them, §4.2.5).
+ * - bf16 is the only element type of K, V, q and outputs (dtype code
+ *   MSGL_DTYPE_BF16); head_dim must be 128; q heads per kv head ("ratio")
+ *   must be 1, 2, 4, 8 or 16.
+ * - Pool layout: one layer's K (and separately V) is `[num_slots, num_kv_heads,
+ *   head_dim]`, head_dim contiguous, kv heads contiguous, consecutive slots
+ *   `cache_row_stride` elements apart.  Pass the layer's K and V base pointers
+ *   (the pages' 6-D pool is [2][layers][pages][page_size][kv_heads][dim]).
+ * - page_table: int32 `[rows, page_table_stride]`; entry (row, j) is the slot
+ *   of token j of the request that owns the row.  With page_size P > 1 the
+ *   caller guarantees that entries inside a page are consecutive slots; results
+ *   are bit-identical to passing P = 1 for the same table.
+ * - Lengths and indices that live in device memory (seq_lens, prefix_lens,
+ *   extend_lens, q_offsets, req_rows, page_table entries, out_loc) are NOT
+ *   range-checked: out-of-range values are undefined behaviour, as in the
+ *   pages' kernels.  Host-side scalars and pointers ARE validated before any
+ *   HIP call; a rejected call enqueues nothing.
+ * - Return value: MSGL_OK (0) or a negative msgl_status.  No exception crosses
+ *   the ABI.  msgl_last_error() returns a thread-local message for the last
+ *   failure on the calling thread (including the source location).
+ */
+#ifndef MSGL_H
+#define MSGL_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum msgl_status {
+  MSGL_OK = 0,
+  MSGL_ERR_NULL = -1,         /* a required pointer is NULL                     */
+  MSGL_ERR_SHAPE = -2,        /* sizes/strides inconsistent or negative         */
+  MSGL_ERR_UNSUPPORTED = -3,  /* dtype, head_dim, ratio or page_size not served */
+  MSGL_ERR_ALIGN = -4,        /* pointer or stride breaks required alignment    */
+  MSGL_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required     */
+  MSGL_ERR_LAUNCH = -6        /* the HIP runtime rejected a kernel launch       */
+} msgl_status;
+
+enum { MSGL_DTYPE_BF16 = 0, MSGL_DTYPE_F32 = 1 };
+enum { MSGL_INDEX_I32 = 0, MSGL_INDEX_I64 = 1 };
+
+/* Library version as major*10000 + minor*100 + patch. */
+int msgl_version(void);
+
+/* Static text for a status code. */
+const char* msgl_status_string(int status);
+
+/* Thread-local description of the last failure on this thread ("" if none). */
+const char* msgl_last_error(void);
+
+/*
+ * msgl_store_kv — k_cache[out_loc[i]] = k_new[i]; v_cache[out_loc[i]] = v_new[i]
+ * for i in [0, n).  A pure byte copy of one row (num_kv_heads * head_dim
+ * elements) per index; every other slot is left untouched.
+ *
+ *   k_cache, v_cache   pool planes of one layer, [num_slots, row] elements,
+ *                      slot s at offset s * cache_row_stride
+ *   k_new, v_new       [n, row] elements, row i at i * new_row_stride
+ *   out_loc            n indices, int32 (index_dtype = MSGL_INDEX_I32) or
+ *                      int64 (MSGL_INDEX_I64); must be distinct and in
+ *                      [0, num_slots)
+ *   row = num_kv_heads * head_dim elements of `dtype` (bf16 or f32).
+ * Vector width follows alignment: 16-byte copies when pointers, strides and
+ * the row size allow, else 8, 4 or 2 bytes (never an error for alignment).
+ * n == 0 enqueues nothing and returns MSGL_OK.
+ */
+int msgl_store_kv(void* k_cache, void* v_cache, int64_t num_slots,
+                  int64_t cache_row_stride, const void* k_new, const void* v_new,
+                  int64_t new_row_stride, const void* out_loc, int32_t index_dtype,
+                  int64_t n, int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                  hipStream_t stream);
+
+/*
+ * msgl_paged_decode — for each request r in [0, batch) and q head h:
+ *   L = seq_lens[r] (keys, INCLUDING the token just stored), row = req_rows[r]
+ *   (or r when req_rows is NULL), g = h / (num_q_heads / num_kv_heads),
+ *   s_j = sm_scale * dot(q[r, h], K[page_table[row, j], g]),  j in [0, L)
+ *   out[r, h]  = sum_j softmax(s)_j * V[page_table[row, j], g]   (bf16)
+ *   lse_out[r, h] = ln sum_j exp(s_j)                           (fp32, optional)
+ * L == 0 gives out = 0 and lse = -inf.
+ *
+ *   out        bf16 [batch, num_q_heads, 128], contiguous
+ *   lse_out    fp32 [batch, num_q_heads] or NULL
+ *   q          bf16 [batch, num_q_heads, 128]; request r at r * q_row_stride
+ *              elements (>= num_q_heads * 128), heads contiguous
+ *   max_seq_len  host upper bound on every seq_lens[r] (sizes grid/workspace)
+ *   split_tokens keys per split-KV chunk (multiple of 32), or 0 for automatic.
+ *              Chunk c of request r covers keys [c*S, min((c+1)*S, L)); requests
+ *              with more than one chunk are recombined with the LSE merge.
+ *   workspace  device scratch of at least msgl_paged_decode_workspace_size(...)
+ *              bytes (may be NULL when that size is 0); contents on entry are
+ *              ignored, 256-byte alignment required.
+ * Deterministic: for fixed inputs and split size the result bits do not depend
+ * on scheduling, on which slots hold the keys, or on page_size.
+ */
+int msgl_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_stride,
+                      const void* k_cache, const void* v_cache, int64_t num_slots,
+                      int64_t cache_row_stride, const int32_t* page_table,
+                      int64_t page_table_stride, const int32_t* req_rows,
+                      const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int32_t max_seq_len, float sm_scale, int32_t split_tokens,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace msgl_paged_decode needs for these host-side sizes
+ * (0 if no request can need more than one chunk).  The split size actually
+ * used is written to *split_tokens_out when it is not NULL. */
+size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_seq_len, int32_t split_tokens,
+                                        int32_t* split_tokens_out);
+
+/*
+ * msgl_paged_extend — causal extend.  Request r has P = prefix_lens[r] cached
+ * keys and E = extend_lens[r] new tokens, whose K/V were already stored into
+ * the pool at page_table[row, P .. P+E-1].  Its queries are rows
+ * q_offsets[r] .. q_offsets[r]+E-1 of q (q_offsets[r+1] - q_offsets[r] == E).
+ * Query i (absolute position P+i) attends keys j in [0, P+i] (bottom-right
+ * aligned causal mask); with P == 0 this is ordinary causal prefill.
+ *
+ *   out        bf16 [T, num_q_heads, 128] contiguous, T = q_offsets[batch]
+ *   lse_out    fp32 [T, num_q_heads] or NULL
+ *   q          bf16 [T, num_q_heads, 128], row t at t * q_row_stride elements
+ *   max_extend_len, max_kv_len   host upper bounds on E and P + E
+ *   causal     must be 1 (the only mode the method uses)
+ *   workspace  reserved; pass NULL / 0 (msgl_paged_extend_workspace_size
+ *              returns the bytes required, currently 0)
+ */
+int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_stride,
+                      const void* k_cache, const void* v_cache, int64_t num_slots,
+                      int64_t cache_row_stride, const int32_t* page_table,
+                      int64_t page_table_stride, const int32_t* req_rows,
+                      const int32_t* prefix_lens, const int32_t* extend_lens,
+                      const int32_t* q_offsets, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int32_t max_extend_len, int32_t max_kv_len, float sm_scale,
+                      int32_t causal, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+size_t msgl_paged_extend_workspace_size(int32_t batch, int32_t num_q_heads,
+                                        int32_t num_kv_heads, int32_t head_dim,
+                                        int32_t max_extend_len, int32_t max_kv_len);
+
+/*
+ * msgl_merge_states — for each (n, h): M = max_s part_lse[s, n, h],
+ *   w_s = exp(part_lse[s, n, h] - M),
+ *   out[n, h] = sum_s w_s part_out[s, n, h] / sum_s w_s,
+ *   lse_out[n, h] = M + ln sum_s w_s.
+ * Parts with lse = -inf carry no weight; if all are -inf the output is 0 and
+ * lse is -inf.
+ *
+ *   part_out   fp32 [num_parts, n, num_heads, head_dim] contiguous
+ *   part_lse   fp32 [num_parts, n, num_heads] contiguous
+ *   out        [n, num_heads, head_dim] of out_dtype (bf16 or f32)
+ *   lse_out    fp32 [n, num_heads] or NULL
+ *   head_dim   multiple of 4, at most 256
+ */
+int msgl_merge_states(void* out, float* lse_out, const float* part_out,
+                      const float* part_lse, int32_t num_parts, int64_t n,
+                      int32_t num_heads, int32_t head_dim, int32_t out_dtype,
+                      hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSGL_H */

@@ -1,0 +1,18 @@
+"""Paged-KV attention for MI355X (gfx950): store_kv, paged decode, extend, merge.
+
+The compute lives in ``libmsgl.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/msgl.h``); this package is the thin ctypes binding.
+"""
+
+from .binding import (  # noqa: F401
+    MsglError,
+    load,
+    version,
+    store_kv,
+    paged_decode,
+    paged_decode_workspace_size,
+    paged_extend,
+    merge_states,
+    alloc_workspace,
+)
+from ._build import LIB_PATH  # noqa: F401

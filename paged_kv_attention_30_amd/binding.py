@@ -1,0 +1,303 @@
+"""Thin Python binding over the libmsgl C ABI (argument marshalling only).
+
+Every function takes torch tensors that already live on the GPU, checks
+dtypes/devices/contiguity, passes raw pointers and sizes to the library and
+enqueues the work on torch's current HIP stream (or the ``stream`` given).
+All computation happens in the HIP kernels; nothing here computes results.
+If the library is missing, loading fails loudly: there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from ._build import LIB_PATH
+
+MSGL_OK = 0
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+INDEX_I32 = 0
+INDEX_I64 = 1
+
+_lib = None
+
+_c_void_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+_f32 = ctypes.c_float
+_size_t = ctypes.c_size_t
+
+SIGNATURES = {
+    "msgl_version": (_i32, []),
+    "msgl_status_string": (ctypes.c_char_p, [_i32]),
+    "msgl_last_error": (ctypes.c_char_p, []),
+    "msgl_store_kv": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64,
+                             _c_void_p, _i32, _i64, _i32, _i32, _i32, _c_void_p]),
+    "msgl_paged_decode": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p,
+                                 _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p, _i32, _i32,
+                                 _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p, _size_t,
+                                 _c_void_p]),
+    "msgl_paged_decode_workspace_size": (_size_t, [_i32, _i32, _i32, _i32, _i32, _i32,
+                                                   ctypes.POINTER(_i32)]),
+    "msgl_paged_extend": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p,
+                                 _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                 _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                 _i32, _c_void_p, _size_t, _c_void_p]),
+    "msgl_paged_extend_workspace_size": (_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "msgl_merge_states": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i32,
+                                 _i32, _i32, _c_void_p]),
+}
+
+
+class MsglError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = load()
+        text = lib.msgl_status_string(status).decode()
+        detail = lib.msgl_last_error().decode()
+        super().__init__(f"{where}: {text} [{detail}]")
+        self.status = status
+
+
+def load(path: str | None = None):
+    """Load libmsgl.so (built by ``__graft_entry__.build()``); raise if absent."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or os.environ.get("MSGL_LIBRARY", LIB_PATH)
+    if not os.path.exists(path):
+        raise RuntimeError(f"libmsgl not built: {path} is missing (run __graft_entry__.build())")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != MSGL_OK:
+        raise MsglError(status, where)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _need(t: torch.Tensor, dtype, name: str, dims=None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dims is not None and t.dim() != dims:
+        raise ValueError(f"{name} must have {dims} dims, got {tuple(t.shape)}")
+
+
+def _pool_geometry(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    """Pool planes are [num_slots, Hkv, D] (heads and dims contiguous)."""
+    _need(k_cache, torch.bfloat16, "k_cache", 3)
+    _need(v_cache, torch.bfloat16, "v_cache", 3)
+    if k_cache.shape != v_cache.shape or k_cache.stride() != v_cache.stride():
+        raise ValueError("k_cache and v_cache must have the same shape and strides")
+    n, hkv, d = k_cache.shape
+    if k_cache.stride(2) != 1 or k_cache.stride(1) != d:
+        raise ValueError("pool rows must hold kv heads x head_dim contiguously")
+    return n, hkv, d, k_cache.stride(0)
+
+
+def version() -> int:
+    return load().msgl_version()
+
+
+# ---------------------------------------------------------------------------
+# store_kv
+# ---------------------------------------------------------------------------
+
+def store_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+             v_new: torch.Tensor, out_loc: torch.Tensor, stream=None) -> None:
+    """k_cache[out_loc[i]] = k_new[i] and likewise for V (in place)."""
+    lib = load()
+    if k_cache.dim() != 3 or k_new.dim() != 3:
+        raise ValueError("k_cache [slots, Hkv, D] and k_new [n, Hkv, D] expected")
+    if k_cache.dtype not in (torch.bfloat16, torch.float32) or k_new.dtype != k_cache.dtype \
+            or v_cache.dtype != k_cache.dtype or v_new.dtype != k_cache.dtype:
+        raise TypeError("pool and new rows must share one dtype (bf16 or f32)")
+    if out_loc.dtype not in (torch.int32, torch.int64):
+        raise TypeError("out_loc must be int32 or int64")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache), ("k_new", k_new),
+                    ("v_new", v_new), ("out_loc", out_loc)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor")
+    n_slots, hkv, d = k_cache.shape
+    if tuple(k_new.shape[1:]) != (hkv, d) or v_new.shape != k_new.shape or v_cache.shape != k_cache.shape:
+        raise ValueError("shape mismatch between pool planes and new rows")
+    for t in (k_cache, v_cache, k_new, v_new):
+        if t.stride(2) != 1 or t.stride(1) != d:
+            raise ValueError("rows must hold kv heads x head_dim contiguously")
+    if k_cache.stride(0) != v_cache.stride(0) or k_new.stride(0) != v_new.stride(0):
+        raise ValueError("K and V planes must share row strides")
+    if out_loc.dim() != 1 or out_loc.shape[0] != k_new.shape[0] or not out_loc.is_contiguous():
+        raise ValueError("out_loc must be a contiguous [n] vector")
+    st = lib.msgl_store_kv(
+        _ptr(k_cache), _ptr(v_cache), n_slots, k_cache.stride(0), _ptr(k_new), _ptr(v_new),
+        k_new.stride(0), _ptr(out_loc), INDEX_I64 if out_loc.dtype == torch.int64 else INDEX_I32,
+        k_new.shape[0], hkv, d, DTYPE_BF16 if k_cache.dtype == torch.bfloat16 else DTYPE_F32,
+        _stream(stream))
+    _check(st, "msgl_store_kv")
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def paged_decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int,
+                                max_seq_len: int, split_tokens: int = 0,
+                                head_dim: int = 128) -> tuple[int, int]:
+    """(bytes, split size used) for a decode call with these host sizes."""
+    lib = load()
+    s = _i32(0)
+    n = lib.msgl_paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
+                                             max_seq_len, split_tokens, ctypes.byref(s))
+    return int(n), int(s.value)
+
+
+def alloc_workspace(nbytes: int, device=None) -> torch.Tensor | None:
+    if nbytes <= 0:
+        return None
+    return torch.empty(nbytes, dtype=torch.uint8, device=device or "cuda")
+
+
+def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                 sm_scale: float, req_rows: torch.Tensor | None = None, page_size: int = 1,
+                 split_tokens: int = 0, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | None = None, want_lse: bool = True,
+                 workspace: torch.Tensor | None = None, stream=None):
+    """Decode attention.  q [B, Hq, 128] bf16 (row stride free, heads contiguous).
+
+    Returns ``(out [B, Hq, 128] bf16, lse [B, Hq] fp32 or None)``.
+    """
+    lib = load()
+    _need(q, torch.bfloat16, "q", 3)
+    n_slots, hkv, d, cstride = _pool_geometry(k_cache, v_cache)
+    B, hq, dq = q.shape
+    if dq != d or q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError("q must be [B, Hq, D] with heads x dims contiguous")
+    _need(page_table, torch.int32, "page_table", 2)
+    _need(seq_lens, torch.int32, "seq_lens", 1)
+    if page_table.stride(1) != 1:
+        raise ValueError("page_table rows must be contiguous")
+    if seq_lens.shape[0] != B or not seq_lens.is_contiguous():
+        raise ValueError("seq_lens must be a contiguous [B] vector")
+    if req_rows is not None:
+        _need(req_rows, torch.int32, "req_rows", 1)
+        if req_rows.shape[0] != B or not req_rows.is_contiguous():
+            raise ValueError("req_rows must be a contiguous [B] vector")
+    if out is None:
+        out = torch.empty((B, hq, d), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out", 3)
+    if not out.is_contiguous() or tuple(out.shape) != (B, hq, d):
+        raise ValueError("out must be a contiguous [B, Hq, D] tensor")
+    if want_lse and lse is None:
+        lse = torch.empty((B, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, torch.float32, "lse", 2)
+        if not lse.is_contiguous() or tuple(lse.shape) != (B, hq):
+            raise ValueError("lse must be a contiguous [B, Hq] tensor")
+    need, _ = paged_decode_workspace_size(B, hq, hkv, max(1, max_seq_len), split_tokens, d)
+    if workspace is None and need:
+        workspace = alloc_workspace(need, q.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    st = lib.msgl_paged_decode(
+        _ptr(out), _ptr(lse), _ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), n_slots, cstride,
+        _ptr(page_table), page_table.stride(0), _ptr(req_rows), _ptr(seq_lens), B, hq, hkv, d,
+        page_size, max_seq_len, float(sm_scale), split_tokens, _ptr(workspace), ws_bytes,
+        _stream(stream))
+    _check(st, "msgl_paged_decode")
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# extend
+# ---------------------------------------------------------------------------
+
+def paged_extend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                 page_table: torch.Tensor, prefix_lens: torch.Tensor,
+                 extend_lens: torch.Tensor, q_offsets: torch.Tensor, max_extend_len: int,
+                 max_kv_len: int, sm_scale: float, req_rows: torch.Tensor | None = None,
+                 page_size: int = 1, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | None = None, want_lse: bool = True, stream=None):
+    """Causal extend.  q [T, Hq, 128] bf16; returns (out [T, Hq, 128], lse [T, Hq])."""
+    lib = load()
+    _need(q, torch.bfloat16, "q", 3)
+    n_slots, hkv, d, cstride = _pool_geometry(k_cache, v_cache)
+    T, hq, dq = q.shape
+    if dq != d or q.stride(2) != 1 or q.stride(1) != d:
+        raise ValueError("q must be [T, Hq, D] with heads x dims contiguous")
+    _need(page_table, torch.int32, "page_table", 2)
+    B = extend_lens.shape[0]
+    for name, t, n in (("prefix_lens", prefix_lens, B), ("extend_lens", extend_lens, B),
+                       ("q_offsets", q_offsets, B + 1)):
+        _need(t, torch.int32, name, 1)
+        if t.shape[0] != n or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [{n}] vector")
+    if req_rows is not None:
+        _need(req_rows, torch.int32, "req_rows", 1)
+        if req_rows.shape[0] != B or not req_rows.is_contiguous():
+            raise ValueError("req_rows must be a contiguous [B] vector")
+    if out is None:
+        out = torch.empty((T, hq, d), dtype=torch.bfloat16, device=q.device)
+    _need(out, torch.bfloat16, "out", 3)
+    if not out.is_contiguous() or tuple(out.shape) != (T, hq, d):
+        raise ValueError("out must be a contiguous [T, Hq, D] tensor")
+    if want_lse and lse is None:
+        lse = torch.empty((T, hq), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _need(lse, torch.float32, "lse", 2)
+        if not lse.is_contiguous() or tuple(lse.shape) != (T, hq):
+            raise ValueError("lse must be a contiguous [T, Hq] tensor")
+    st = lib.msgl_paged_extend(
+        _ptr(out), _ptr(lse), _ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), n_slots, cstride,
+        _ptr(page_table), page_table.stride(0), _ptr(req_rows), _ptr(prefix_lens),
+        _ptr(extend_lens), _ptr(q_offsets), B, hq, hkv, d, page_size, max_extend_len, max_kv_len,
+        float(sm_scale), 1, None, 0, _stream(stream))
+    _check(st, "msgl_paged_extend")
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# merge
+# ---------------------------------------------------------------------------
+
+def merge_states(part_out: torch.Tensor, part_lse: torch.Tensor,
+                 out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                 lse: torch.Tensor | None = None, want_lse: bool = True, stream=None):
+    """part_out [S, N, H, D] fp32, part_lse [S, N, H] fp32 -> (out [N, H, D], lse [N, H])."""
+    lib = load()
+    _need(part_out, torch.float32, "part_out", 4)
+    _need(part_lse, torch.float32, "part_lse", 3)
+    if not part_out.is_contiguous() or not part_lse.is_contiguous():
+        raise ValueError("partials must be contiguous")
+    S, N, H, D = part_out.shape
+    if tuple(part_lse.shape) != (S, N, H):
+        raise ValueError("part_lse must be [S, N, H]")
+    if out is None:
+        out = torch.empty((N, H, D), dtype=out_dtype, device=part_out.device)
+    if want_lse and lse is None:
+        lse = torch.empty((N, H), dtype=torch.float32, device=part_out.device)
+    code = DTYPE_BF16 if out.dtype == torch.bfloat16 else DTYPE_F32
+    st = lib.msgl_merge_states(_ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse), S, N, H, D,
+                               code, _stream(stream))
+    _check(st, "msgl_merge_states")
+    return out, lse

@@ -1,0 +1,343 @@
+// C ABI of the library: host-side validation, planning and dispatch.
+//
+// Every entry point validates its host-visible arguments first (pointers,
+// sizes, strides, alignment, workspace) and returns a status code without
+// touching the HIP runtime when something is wrong, in the spirit of the
+// declarative shape checks the pages describe for their store kernel
+// ("Mini-SGLang complete analysis" §4.9.4: one symbolic size bound across
+// several tensors, a failure reports where it happened).
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/msgl.h"
+#include "internal.hpp"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* file, int line, const char* fmt, ...) {
+  char msg[400];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(msg, sizeof(msg), fmt, ap);
+  va_end(ap);
+  const char* base = strrchr(file, '/');
+  snprintf(g_last_error, sizeof(g_last_error), "%s (%s:%d)", msg, base ? base + 1 : file, line);
+  return status;
+}
+
+#define MSGL_FAIL(status, ...) fail((status), __FILE__, __LINE__, __VA_ARGS__)
+#define MSGL_CHECK(cond, status, ...) \
+  do {                                \
+    if (!(cond)) return MSGL_FAIL((status), __VA_ARGS__); \
+  } while (0)
+
+constexpr int kHeadDim = 128;
+constexpr int kDefaultSplit = 256;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool ratio_ok(int hq, int hkv) {
+  if (hkv <= 0 || hq <= 0 || hq % hkv) return false;
+  const int r = hq / hkv;
+  return r == 1 || r == 2 || r == 4 || r == 8 || r == 16;
+}
+
+int launch_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MSGL_OK;
+  return MSGL_FAIL(MSGL_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
+}
+
+// Split size: keep at least ~4 chunks of work per compute unit when the
+// batch is small, never below 64 keys; the value depends on host sizes only.
+int32_t resolve_split(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
+                      int32_t requested) {
+  if (requested > 0) return requested;
+  (void)num_kv_heads;
+  (void)batch;
+  (void)max_seq_len;
+  return kDefaultSplit;
+}
+
+int validate_pool(const void* k_cache, const void* v_cache, int64_t num_slots,
+                  int64_t cache_row_stride, int32_t num_kv_heads, int32_t head_dim) {
+  MSGL_CHECK(k_cache && v_cache, MSGL_ERR_NULL, "k_cache/v_cache is NULL");
+  MSGL_CHECK(head_dim == kHeadDim, MSGL_ERR_UNSUPPORTED, "head_dim %d unsupported (only 128)", head_dim);
+  MSGL_CHECK(num_kv_heads > 0, MSGL_ERR_SHAPE, "num_kv_heads %d must be positive", num_kv_heads);
+  MSGL_CHECK(num_slots > 0, MSGL_ERR_SHAPE, "num_slots %lld must be positive", (long long)num_slots);
+  MSGL_CHECK(cache_row_stride >= (int64_t)num_kv_heads * head_dim, MSGL_ERR_SHAPE,
+             "cache_row_stride %lld < num_kv_heads*head_dim %lld", (long long)cache_row_stride,
+             (long long)num_kv_heads * head_dim);
+  MSGL_CHECK(aligned(k_cache, 16) && aligned(v_cache, 16), MSGL_ERR_ALIGN,
+             "k_cache/v_cache must be 16-byte aligned");
+  MSGL_CHECK((cache_row_stride * 2) % 16 == 0, MSGL_ERR_ALIGN,
+             "cache_row_stride*2 bytes must be a multiple of 16");
+  return MSGL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msgl_version(void) { return 100; }
+
+const char* msgl_status_string(int status) {
+  switch (status) {
+    case MSGL_OK: return "MSGL_OK";
+    case MSGL_ERR_NULL: return "MSGL_ERR_NULL: a required pointer is NULL";
+    case MSGL_ERR_SHAPE: return "MSGL_ERR_SHAPE: inconsistent or negative sizes/strides";
+    case MSGL_ERR_UNSUPPORTED: return "MSGL_ERR_UNSUPPORTED: dtype, head_dim, ratio or page_size not served";
+    case MSGL_ERR_ALIGN: return "MSGL_ERR_ALIGN: pointer or stride breaks required alignment";
+    case MSGL_ERR_WORKSPACE: return "MSGL_ERR_WORKSPACE: workspace missing or too small";
+    case MSGL_ERR_LAUNCH: return "MSGL_ERR_LAUNCH: the HIP runtime rejected a launch";
+    default: return "unknown msgl status";
+  }
+}
+
+const char* msgl_last_error(void) { return g_last_error; }
+
+int msgl_store_kv(void* k_cache, void* v_cache, int64_t num_slots, int64_t cache_row_stride,
+                  const void* k_new, const void* v_new, int64_t new_row_stride,
+                  const void* out_loc, int32_t index_dtype, int64_t n, int32_t num_kv_heads,
+                  int32_t head_dim, int32_t dtype, hipStream_t stream) {
+  g_last_error[0] = 0;
+  MSGL_CHECK(n >= 0, MSGL_ERR_SHAPE, "n %lld is negative", (long long)n);
+  MSGL_CHECK(dtype == MSGL_DTYPE_BF16 || dtype == MSGL_DTYPE_F32, MSGL_ERR_UNSUPPORTED,
+             "dtype %d unsupported", dtype);
+  MSGL_CHECK(index_dtype == MSGL_INDEX_I32 || index_dtype == MSGL_INDEX_I64, MSGL_ERR_UNSUPPORTED,
+             "index dtype %d unsupported", index_dtype);
+  MSGL_CHECK(num_kv_heads > 0 && head_dim > 0, MSGL_ERR_SHAPE, "num_kv_heads/head_dim must be positive");
+  MSGL_CHECK(num_slots > 0, MSGL_ERR_SHAPE, "num_slots must be positive");
+  const int64_t row = (int64_t)num_kv_heads * head_dim;
+  MSGL_CHECK(cache_row_stride >= row, MSGL_ERR_SHAPE, "cache_row_stride %lld < row %lld",
+             (long long)cache_row_stride, (long long)row);
+  MSGL_CHECK(new_row_stride >= row, MSGL_ERR_SHAPE, "new_row_stride %lld < row %lld",
+             (long long)new_row_stride, (long long)row);
+  if (n == 0) return MSGL_OK;
+  MSGL_CHECK(k_cache && v_cache && k_new && v_new && out_loc, MSGL_ERR_NULL,
+             "k_cache, v_cache, k_new, v_new and out_loc must be non-NULL");
+  const int esz = dtype == MSGL_DTYPE_BF16 ? 2 : 4;
+  MSGL_CHECK(aligned(k_cache, esz) && aligned(v_cache, esz) && aligned(k_new, esz) &&
+                 aligned(v_new, esz),
+             MSGL_ERR_ALIGN, "tensors must be aligned to their element size");
+  MSGL_CHECK(aligned(out_loc, index_dtype == MSGL_INDEX_I64 ? 8 : 4), MSGL_ERR_ALIGN,
+             "out_loc must be aligned to its element size");
+
+  msgl::StoreArgs a;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cache_stride_bytes = cache_row_stride * esz;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.new_stride_bytes = new_row_stride * esz;
+  a.out_loc = out_loc;
+  a.index_is_i64 = index_dtype == MSGL_INDEX_I64;
+  a.n = n;
+  a.row_bytes = row * esz;
+  a.stream = stream;
+  int unit = 16;
+  while (unit > esz) {
+    const bool ok = aligned(k_cache, unit) && aligned(v_cache, unit) && aligned(k_new, unit) &&
+                    aligned(v_new, unit) && a.cache_stride_bytes % unit == 0 &&
+                    a.new_stride_bytes % unit == 0 && a.row_bytes % unit == 0;
+    if (ok) break;
+    unit /= 2;
+  }
+  a.unit_bytes = unit;
+  return launch_status(msgl::launch_store_kv(a), "store_kv");
+}
+
+size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_seq_len,
+                                        int32_t split_tokens, int32_t* split_tokens_out) {
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) {
+    if (split_tokens_out) *split_tokens_out = 0;
+    return 0;
+  }
+  const int32_t S = resolve_split(batch, num_kv_heads, max_seq_len, split_tokens);
+  if (split_tokens_out) *split_tokens_out = S;
+  const int64_t splits = ((int64_t)max_seq_len + S - 1) / S;
+  if (splits <= 1) return 0;
+  const int64_t rows = splits * batch * num_q_heads;
+  size_t bytes = (size_t)rows * head_dim * sizeof(float);
+  bytes = (bytes + 255) / 256 * 256;
+  bytes += (size_t)rows * sizeof(float);
+  return (bytes + 255) / 256 * 256;
+}
+
+int msgl_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_stride,
+                      const void* k_cache, const void* v_cache, int64_t num_slots,
+                      int64_t cache_row_stride, const int32_t* page_table,
+                      int64_t page_table_stride, const int32_t* req_rows,
+                      const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int32_t max_seq_len, float sm_scale, int32_t split_tokens,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_last_error[0] = 0;
+  MSGL_CHECK(batch >= 0, MSGL_ERR_SHAPE, "batch %d is negative", batch);
+  int st = validate_pool(k_cache, v_cache, num_slots, cache_row_stride, num_kv_heads, head_dim);
+  if (st) return st;
+  MSGL_CHECK(ratio_ok(num_q_heads, num_kv_heads), MSGL_ERR_UNSUPPORTED,
+             "num_q_heads %d / num_kv_heads %d: ratio must be 1, 2, 4, 8 or 16", num_q_heads,
+             num_kv_heads);
+  MSGL_CHECK(page_size >= 1, MSGL_ERR_UNSUPPORTED, "page_size %d must be >= 1", page_size);
+  MSGL_CHECK(max_seq_len >= 0, MSGL_ERR_SHAPE, "max_seq_len %d is negative", max_seq_len);
+  MSGL_CHECK(split_tokens >= 0 && split_tokens % 32 == 0, MSGL_ERR_SHAPE,
+             "split_tokens %d must be 0 or a positive multiple of 32", split_tokens);
+  MSGL_CHECK(q_row_stride >= (int64_t)num_q_heads * head_dim, MSGL_ERR_SHAPE,
+             "q_row_stride %lld < num_q_heads*head_dim", (long long)q_row_stride);
+  MSGL_CHECK(page_table_stride >= max_seq_len, MSGL_ERR_SHAPE,
+             "page_table_stride %lld < max_seq_len %d", (long long)page_table_stride, max_seq_len);
+  if (batch == 0) return MSGL_OK;
+  MSGL_CHECK(out && q && page_table && seq_lens, MSGL_ERR_NULL,
+             "out, q, page_table and seq_lens must be non-NULL");
+  MSGL_CHECK(aligned(q, 16) && aligned(out, 16), MSGL_ERR_ALIGN, "q and out must be 16-byte aligned");
+  MSGL_CHECK((q_row_stride * 2) % 16 == 0, MSGL_ERR_ALIGN, "q_row_stride*2 must be a multiple of 16");
+  MSGL_CHECK(aligned(page_table, 4) && aligned(seq_lens, 4) && (!req_rows || aligned(req_rows, 4)) &&
+                 (!lse_out || aligned(lse_out, 4)),
+             MSGL_ERR_ALIGN, "int32/fp32 arrays must be 4-byte aligned");
+
+  int32_t S = 0;
+  const size_t need = msgl_paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
+                                                       max_seq_len > 0 ? max_seq_len : 1,
+                                                       split_tokens, &S);
+  MSGL_CHECK(workspace_bytes >= need, MSGL_ERR_WORKSPACE, "workspace %zu bytes < required %zu",
+             workspace_bytes, need);
+  MSGL_CHECK(need == 0 || (workspace && aligned(workspace, 256)), MSGL_ERR_WORKSPACE,
+             "workspace must be non-NULL and 256-byte aligned");
+
+  msgl::DecodeArgs a;
+  a.out = out;
+  a.lse = lse_out;
+  a.q = q;
+  a.q_stride = q_row_stride;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cache_stride = cache_row_stride;
+  a.page_table = page_table;
+  a.pt_stride = page_table_stride;
+  a.req_rows = req_rows;
+  a.seq_lens = seq_lens;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.page_size = page_size;
+  a.max_seq_len = max_seq_len;
+  a.sm_scale = sm_scale;
+  a.stream = stream;
+  a.split_tokens = S;
+  a.max_splits = max_seq_len > 0 ? (int32_t)(((int64_t)max_seq_len + S - 1) / S) : 1;
+  const int64_t rows = (int64_t)a.max_splits * batch * num_q_heads;
+  a.part_out = need ? (float*)workspace : nullptr;
+  a.part_lse = need ? (float*)((char*)workspace + ((size_t)rows * head_dim * 4 + 255) / 256 * 256)
+                    : nullptr;
+  if (!need) a.max_splits = 1;
+  return launch_status(msgl::launch_paged_decode(a), "paged_decode");
+}
+
+size_t msgl_paged_extend_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                        int32_t head_dim, int32_t max_extend_len,
+                                        int32_t max_kv_len) {
+  (void)batch; (void)num_q_heads; (void)num_kv_heads; (void)head_dim;
+  (void)max_extend_len; (void)max_kv_len;
+  return 0;
+}
+
+int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_stride,
+                      const void* k_cache, const void* v_cache, int64_t num_slots,
+                      int64_t cache_row_stride, const int32_t* page_table,
+                      int64_t page_table_stride, const int32_t* req_rows,
+                      const int32_t* prefix_lens, const int32_t* extend_lens,
+                      const int32_t* q_offsets, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int32_t max_extend_len, int32_t max_kv_len, float sm_scale,
+                      int32_t causal, void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  g_last_error[0] = 0;
+  (void)workspace;
+  (void)workspace_bytes;
+  MSGL_CHECK(batch >= 0, MSGL_ERR_SHAPE, "batch %d is negative", batch);
+  int st = validate_pool(k_cache, v_cache, num_slots, cache_row_stride, num_kv_heads, head_dim);
+  if (st) return st;
+  MSGL_CHECK(ratio_ok(num_q_heads, num_kv_heads), MSGL_ERR_UNSUPPORTED,
+             "num_q_heads %d / num_kv_heads %d: ratio must be 1, 2, 4, 8 or 16", num_q_heads,
+             num_kv_heads);
+  MSGL_CHECK(causal == 1, MSGL_ERR_UNSUPPORTED, "only causal extend (causal=1) is served");
+  MSGL_CHECK(page_size >= 1, MSGL_ERR_UNSUPPORTED, "page_size %d must be >= 1", page_size);
+  MSGL_CHECK(max_extend_len >= 0 && max_kv_len >= max_extend_len, MSGL_ERR_SHAPE,
+             "need 0 <= max_extend_len <= max_kv_len");
+  MSGL_CHECK(q_row_stride >= (int64_t)num_q_heads * head_dim, MSGL_ERR_SHAPE,
+             "q_row_stride %lld < num_q_heads*head_dim", (long long)q_row_stride);
+  MSGL_CHECK(page_table_stride >= max_kv_len, MSGL_ERR_SHAPE,
+             "page_table_stride %lld < max_kv_len %d", (long long)page_table_stride, max_kv_len);
+  if (batch == 0 || max_extend_len == 0) return MSGL_OK;
+  MSGL_CHECK(out && q && page_table && prefix_lens && extend_lens && q_offsets, MSGL_ERR_NULL,
+             "out, q, page_table, prefix_lens, extend_lens and q_offsets must be non-NULL");
+  MSGL_CHECK(aligned(q, 16) && aligned(out, 16), MSGL_ERR_ALIGN, "q and out must be 16-byte aligned");
+  MSGL_CHECK((q_row_stride * 2) % 16 == 0, MSGL_ERR_ALIGN, "q_row_stride*2 must be a multiple of 16");
+  MSGL_CHECK(aligned(page_table, 4) && aligned(prefix_lens, 4) && aligned(extend_lens, 4) &&
+                 aligned(q_offsets, 4) && (!req_rows || aligned(req_rows, 4)) &&
+                 (!lse_out || aligned(lse_out, 4)),
+             MSGL_ERR_ALIGN, "int32/fp32 arrays must be 4-byte aligned");
+
+  msgl::ExtendArgs a;
+  a.out = out;
+  a.lse = lse_out;
+  a.q = q;
+  a.q_stride = q_row_stride;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cache_stride = cache_row_stride;
+  a.page_table = page_table;
+  a.pt_stride = page_table_stride;
+  a.req_rows = req_rows;
+  a.prefix_lens = prefix_lens;
+  a.extend_lens = extend_lens;
+  a.q_offsets = q_offsets;
+  a.batch = batch;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.page_size = page_size;
+  a.max_extend_len = max_extend_len;
+  a.max_kv_len = max_kv_len;
+  a.sm_scale = sm_scale;
+  a.stream = stream;
+  return launch_status(msgl::launch_paged_extend(a), "paged_extend");
+}
+
+int msgl_merge_states(void* out, float* lse_out, const float* part_out, const float* part_lse,
+                      int32_t num_parts, int64_t n, int32_t num_heads, int32_t head_dim,
+                      int32_t out_dtype, hipStream_t stream) {
+  g_last_error[0] = 0;
+  MSGL_CHECK(num_parts >= 1, MSGL_ERR_SHAPE, "num_parts %d must be >= 1", num_parts);
+  MSGL_CHECK(n >= 0 && num_heads > 0, MSGL_ERR_SHAPE, "n must be >= 0 and num_heads > 0");
+  MSGL_CHECK(head_dim > 0 && head_dim % 4 == 0 && head_dim <= 256, MSGL_ERR_UNSUPPORTED,
+             "head_dim %d must be a positive multiple of 4, at most 256", head_dim);
+  MSGL_CHECK(out_dtype == MSGL_DTYPE_BF16 || out_dtype == MSGL_DTYPE_F32, MSGL_ERR_UNSUPPORTED,
+             "out dtype %d unsupported", out_dtype);
+  MSGL_CHECK(n <= 0x7fffffffLL, MSGL_ERR_SHAPE, "n too large");
+  if (n == 0) return MSGL_OK;
+  MSGL_CHECK(out && part_out && part_lse, MSGL_ERR_NULL, "out, part_out and part_lse must be non-NULL");
+  MSGL_CHECK(aligned(part_out, 16) && aligned(part_lse, 4) && aligned(out, 16) &&
+                 (!lse_out || aligned(lse_out, 4)),
+             MSGL_ERR_ALIGN, "part_out/out must be 16-byte aligned, lse arrays 4-byte aligned");
+  msgl::MergeArgs a;
+  a.out = out;
+  a.lse = lse_out;
+  a.part_out = part_out;
+  a.part_lse = part_lse;
+  a.num_parts = num_parts;
+  a.n = n;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.out_bf16 = out_dtype == MSGL_DTYPE_BF16;
+  a.seq_lens = nullptr;
+  a.split_tokens = 0;
+  a.stream = stream;
+  return launch_status(msgl::launch_merge(a), "merge_states");
+}
+
+}  // extern "C"

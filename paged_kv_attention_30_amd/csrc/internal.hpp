@@ -1,0 +1,101 @@
+// Host-side argument bundles and kernel launchers (library-internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace msgl {
+
+template <int W> struct VecOf;
+template <> struct VecOf<16> { typedef uint4 type; };
+template <> struct VecOf<8> { typedef uint2 type; };
+template <> struct VecOf<4> { typedef uint32_t type; };
+template <> struct VecOf<2> { typedef uint16_t type; };
+
+struct StoreArgs {
+  void* k_cache;
+  void* v_cache;
+  int64_t cache_stride_bytes;
+  const void* k_new;
+  const void* v_new;
+  int64_t new_stride_bytes;
+  const void* out_loc;
+  bool index_is_i64;
+  int64_t n;
+  int64_t row_bytes;
+  int unit_bytes;  // 16, 8, 4 or 2: widest unit every address is aligned to
+  hipStream_t stream;
+};
+
+struct DecodeArgs {
+  void* out;               // bf16 [B, Hq, 128]
+  float* lse;              // fp32 [B, Hq] or null
+  const void* q;           // bf16, row stride q_stride elements
+  int64_t q_stride;
+  const void* k_cache;
+  const void* v_cache;
+  int64_t cache_stride;    // elements between slots
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const int32_t* req_rows; // null -> identity
+  const int32_t* seq_lens;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t max_seq_len;
+  float sm_scale;
+  int32_t split_tokens;    // resolved (> 0)
+  int32_t max_splits;      // ceil(max_seq_len / split_tokens)
+  float* part_out;         // fp32 [max_splits, B, Hq, 128] (when max_splits > 1)
+  float* part_lse;         // fp32 [max_splits, B, Hq]
+  hipStream_t stream;
+};
+
+struct ExtendArgs {
+  void* out;               // bf16 [T, Hq, 128]
+  float* lse;              // fp32 [T, Hq] or null
+  const void* q;
+  int64_t q_stride;
+  const void* k_cache;
+  const void* v_cache;
+  int64_t cache_stride;
+  const int32_t* page_table;
+  int64_t pt_stride;
+  const int32_t* req_rows;
+  const int32_t* prefix_lens;
+  const int32_t* extend_lens;
+  const int32_t* q_offsets;
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t max_extend_len;
+  int32_t max_kv_len;
+  float sm_scale;
+  hipStream_t stream;
+};
+
+struct MergeArgs {
+  void* out;
+  float* lse;
+  const float* part_out;   // [S, N, H, D]
+  const float* part_lse;   // [S, N, H]
+  int32_t num_parts;
+  int64_t n;
+  int32_t num_heads;
+  int32_t head_dim;
+  bool out_bf16;
+  // decode-internal use: per-row part counts from seq_lens (else num_parts)
+  const int32_t* seq_lens;
+  int32_t split_tokens;
+  hipStream_t stream;
+};
+
+hipError_t launch_store_kv(const StoreArgs& a);
+hipError_t launch_paged_decode(const DecodeArgs& a);
+hipError_t launch_paged_extend(const ExtendArgs& a);
+hipError_t launch_merge(const MergeArgs& a);
+
+}  // namespace msgl

@@ -1,0 +1,185 @@
+"""The C ABI: symbols, status strings and host-side validation (CPU only).
+
+Validation runs before any HIP call, so every rejected call below returns
+its status code on a machine without a GPU.  Pointers passed here are fake
+(never dereferenced); calls that would pass validation are not made.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_kv_attention_30_amd as msgl
+from paged_kv_attention_30_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msgl.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH = 0, -1, -2, -3, -4, -5, -6
+FAKE = 0x10000          # 64 KiB-aligned fake device address, never touched
+FAKE2 = 0x20000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(msgl_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return msgl.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = declared_functions()
+    assert len(names) >= 9
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in msgl.h but not exported"
+        assert name in binding.SIGNATURES, f"{name} has no ctypes signature"
+
+
+def test_status_strings_and_version(lib):
+    assert lib.msgl_version() >= 100
+    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH):
+        assert lib.msgl_status_string(code)
+    assert b"unknown" in lib.msgl_status_string(-99)
+
+
+def decode(lib, **kw):
+    args = dict(out=FAKE, lse=FAKE, q=FAKE, q_stride=32 * 128, k=FAKE, v=FAKE2, slots=1024,
+                cstride=8 * 128, pt=FAKE, pt_stride=4096, rows=None, lens=FAKE, batch=4, hq=32,
+                hkv=8, d=128, page=1, max_len=4096, scale=0.088, split=0, ws=None, ws_bytes=0)
+    args.update(kw)
+    return lib.msgl_paged_decode(args["out"], args["lse"], args["q"], args["q_stride"], args["k"],
+                                 args["v"], args["slots"], args["cstride"], args["pt"],
+                                 args["pt_stride"], args["rows"], args["lens"], args["batch"],
+                                 args["hq"], args["hkv"], args["d"], args["page"], args["max_len"],
+                                 args["scale"], args["split"], args["ws"], args["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), NULL),
+    (dict(out=None), NULL),
+    (dict(lens=None), NULL),
+    (dict(d=64), UNSUP),
+    (dict(hq=24), UNSUP),            # ratio 3
+    (dict(hq=7), UNSUP),             # not a multiple of hkv
+    (dict(hkv=0), SHAPE),
+    (dict(batch=-1), SHAPE),
+    (dict(cstride=100), SHAPE),
+    (dict(q_stride=1000), SHAPE),
+    (dict(pt_stride=100), SHAPE),
+    (dict(split=48), SHAPE),
+    (dict(page=0), UNSUP),
+    (dict(k=FAKE + 2), ALIGN),
+    (dict(q=FAKE + 4), ALIGN),
+    (dict(cstride=8 * 128 + 4), ALIGN),
+    (dict(ws=None, ws_bytes=0), WS),           # 4096 keys need more than one chunk
+    (dict(ws=FAKE + 64, ws_bytes=1 << 30), WS),  # misaligned workspace
+])
+def test_decode_validation(lib, kw, code):
+    st = decode(lib, **kw)
+    assert st == code, (st, lib.msgl_last_error())
+    assert lib.msgl_last_error()  # a message with a source location
+    assert b"api.hip" in lib.msgl_last_error()
+
+
+def test_decode_empty_batch_is_a_no_op(lib):
+    assert decode(lib, batch=0) == OK
+
+
+def test_decode_workspace_size_rule(lib):
+    n, s = msgl.paged_decode_workspace_size(64, 32, 8, 4096, 0)
+    assert s > 0 and s % 32 == 0
+    chunks = -(-4096 // s)
+    assert n >= chunks * 64 * 32 * (128 + 1) * 4
+    assert msgl.paged_decode_workspace_size(64, 32, 8, 200, 256)[0] == 0      # one chunk
+    assert msgl.paged_decode_workspace_size(0, 32, 8, 200, 256)[0] == 0
+
+
+def extend(lib, **kw):
+    args = dict(out=FAKE, lse=FAKE, q=FAKE, q_stride=32 * 128, k=FAKE, v=FAKE2, slots=1024,
+                cstride=8 * 128, pt=FAKE, pt_stride=4096, rows=None, pre=FAKE, ext=FAKE, off=FAKE,
+                batch=2, hq=32, hkv=8, d=128, page=1, max_ext=512, max_kv=4096, scale=0.088,
+                causal=1)
+    args.update(kw)
+    return lib.msgl_paged_extend(args["out"], args["lse"], args["q"], args["q_stride"], args["k"],
+                                 args["v"], args["slots"], args["cstride"], args["pt"],
+                                 args["pt_stride"], args["rows"], args["pre"], args["ext"],
+                                 args["off"], args["batch"], args["hq"], args["hkv"], args["d"],
+                                 args["page"], args["max_ext"], args["max_kv"], args["scale"],
+                                 args["causal"], None, 0, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(causal=0), UNSUP),
+    (dict(pre=None), NULL),
+    (dict(off=None), NULL),
+    (dict(max_kv=100), SHAPE),
+    (dict(pt_stride=1000), SHAPE),
+    (dict(d=256), UNSUP),
+    (dict(hq=40), UNSUP),
+    (dict(out=FAKE + 8), ALIGN),
+    (dict(batch=-2), SHAPE),
+])
+def test_extend_validation(lib, kw, code):
+    st = extend(lib, **kw)
+    assert st == code, (st, lib.msgl_last_error())
+
+
+def test_extend_zero_length_is_a_no_op(lib):
+    assert extend(lib, max_ext=0) == OK
+    assert extend(lib, batch=0) == OK
+
+
+def test_store_validation(lib):
+    def store(**kw):
+        a = dict(k=FAKE, v=FAKE2, slots=1024, cstride=1024, kn=FAKE, vn=FAKE2, nstride=1024,
+                 loc=FAKE, idx=0, n=4, hkv=8, d=128, dtype=0)
+        a.update(kw)
+        return lib.msgl_store_kv(a["k"], a["v"], a["slots"], a["cstride"], a["kn"], a["vn"],
+                                 a["nstride"], a["loc"], a["idx"], a["n"], a["hkv"], a["d"],
+                                 a["dtype"], None)
+    assert store(n=0) == OK
+    assert store(n=-1) == SHAPE
+    assert store(loc=None) == NULL
+    assert store(dtype=7) == UNSUP
+    assert store(idx=3) == UNSUP
+    assert store(cstride=512) == SHAPE
+    assert store(nstride=512) == SHAPE
+    assert store(k=FAKE + 1) == ALIGN
+    assert store(loc=FAKE + 2) == ALIGN
+    assert store(idx=1, loc=FAKE + 4) == ALIGN
+
+
+def test_merge_validation(lib):
+    def merge(**kw):
+        a = dict(out=FAKE, lse=FAKE, po=FAKE, pl=FAKE2, parts=3, n=5, h=8, d=128, dt=0)
+        a.update(kw)
+        return lib.msgl_merge_states(a["out"], a["lse"], a["po"], a["pl"], a["parts"], a["n"],
+                                     a["h"], a["d"], a["dt"], None)
+    assert merge(n=0) == OK
+    assert merge(parts=0) == SHAPE
+    assert merge(d=130) == UNSUP
+    assert merge(d=512) == UNSUP
+    assert merge(dt=5) == UNSUP
+    assert merge(po=None) == NULL
+    assert merge(po=FAKE + 4) == ALIGN
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(2, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        msgl.paged_decode(q, q, q, torch.zeros(2, 4, dtype=torch.int32),
+                          torch.ones(2, dtype=torch.int32), 4, 0.1)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(binding, "_lib", None)
+    with pytest.raises(RuntimeError, match="not built"):
+        binding.load(str(tmp_path / "nope.so"))
+    monkeypatch.setattr(binding, "_lib", None)
+    binding.load()

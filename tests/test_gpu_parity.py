@@ -1,0 +1,353 @@
+"""GPU parity of the HIP kernels against the fp64 CPU oracle (small shapes).
+
+Sizes are chosen so the oracle finishes in seconds while the kernels still
+see several tiles, a ragged tail and the edge cases (one key, exact tile
+multiples, empty work).  Bars: store_kv and indexing invariants bit-exact;
+attention within max abs 2e-2 and max abs / max |ref| 1e-2.
+"""
+
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_attention_30_amd as msgl
+from workloads import small_decode, small_extend, random_bf16, config_c1
+from tests.gpu_util import (Uploaded, up, bits, f64, assert_close, assert_lse_close)
+
+pytestmark = pytest.mark.gpu
+
+
+def banner(msg):
+    print(f"[gpu] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def oracle_pool(inp):
+    return oracle.store_kv(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.out_loc)
+
+
+def oracle_decode(inp, kp, vp):
+    return oracle.paged_decode(inp.dec_q, kp, vp, inp.page_table, inp.dec_req_rows,
+                               inp.dec_seq_lens, inp.sm_scale, inp.num_kv_heads)
+
+
+def oracle_extend(inp, kp, vp):
+    return oracle.paged_extend(inp.ext_q, kp, vp, inp.page_table, inp.ext_req_rows,
+                               inp.ext_prefix_lens, inp.ext_extend_lens, inp.ext_q_offsets,
+                               inp.sm_scale, inp.num_kv_heads)
+
+
+# ---------------------------------------------------------------------------
+# store_kv
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("index_dtype", [np.int32, np.int64])
+def test_store_kv_bit_exact_c1(index_dtype):
+    banner(f"store_kv C1 index {index_dtype.__name__}")
+    inp = config_c1()
+    u = Uploaded(inp)
+    u.out_loc = up(inp.out_loc.astype(index_dtype))
+    u.store()
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    assert np.array_equal(bits(u.k), kp) and np.array_equal(bits(u.v), vp)
+
+
+@pytest.mark.parametrize("n", [1, 3, 257, 4000])
+def test_store_kv_strided_rows_and_ragged_counts(n):
+    banner(f"store_kv strided n={n}")
+    rng = np.random.default_rng(n)
+    slots, hkv, d = 8192, 8, 128
+    k = random_bf16(rng, (slots, hkv, d)); v = random_bf16(rng, (slots, hkv, d))
+    # new rows as views into a wider [n, 3, Hkv, D] buffer (as a fused qkv split would give)
+    fused = random_bf16(rng, (n, 3, hkv, d))
+    loc = rng.permutation(slots)[:n].astype(np.int64)
+    kg, vg = up(k), up(v)
+    fg = up(fused)
+    msgl.store_kv(kg, vg, fg[:, 1], fg[:, 2], up(loc))
+    torch.cuda.synchronize()
+    kp, vp = oracle.store_kv(k, v, fused[:, 1], fused[:, 2], loc)
+    assert np.array_equal(bits(kg), kp) and np.array_equal(bits(vg), vp)
+
+
+def test_store_kv_fp32_and_narrow_rows():
+    banner("store_kv fp32 / odd row size")
+    rng = np.random.default_rng(5)
+    k = rng.standard_normal((300, 3, 6)).astype(np.float32)   # 72-byte rows -> 8-byte units
+    v = rng.standard_normal((300, 3, 6)).astype(np.float32)
+    kn = rng.standard_normal((17, 3, 6)).astype(np.float32)
+    vn = rng.standard_normal((17, 3, 6)).astype(np.float32)
+    loc = rng.permutation(300)[:17].astype(np.int32)
+    kg, vg = up(k), up(v)
+    msgl.store_kv(kg, vg, up(kn), up(vn), up(loc))
+    torch.cuda.synchronize()
+    kp, vp = oracle.store_kv(k, v, kn, vn, loc)
+    assert np.array_equal(kg.cpu().numpy(), kp) and np.array_equal(vg.cpu().numpy(), vp)
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def test_decode_c1_full():
+    banner("decode C1")
+    inp = config_c1()
+    u = Uploaded(inp)
+    u.store()
+    out, lse = u.decode()
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle_decode(inp, kp, vp)
+    assert_close(out, ro, "C1 out")
+    assert_lse_close(lse, rl, "C1 lse")
+
+
+DECODE_CASES = [
+    # (hq, hkv, seq_lens, split_tokens)
+    (8, 8, [1, 31, 32, 33], 0),
+    (16, 8, [64, 65, 255, 256, 257, 600], 0),
+    (32, 8, [700, 1, 129, 1024, 513], 64),
+    (32, 8, [700, 1, 129, 1024, 513], 96),
+    (64, 8, [1500, 2048, 3, 777], 256),
+    (16, 1, [300, 45], 32),
+    (32, 2, [90, 1000, 1001], 128),
+    (4, 2, [5, 40], 0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(DECODE_CASES)))
+def test_decode_parity(case):
+    hq, hkv, lens, split = DECODE_CASES[case]
+    banner(f"decode hq={hq} hkv={hkv} lens={lens} split={split}")
+    inp = small_decode(40 + case, hq, hkv, lens, num_slots=8192)
+    u = Uploaded(inp)
+    u.store()
+    out, lse = u.decode(split_tokens=split)
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle_decode(inp, kp, vp)
+    assert_close(out, ro, f"decode case {case}")
+    assert_lse_close(lse, rl, f"decode case {case}")
+
+
+def test_decode_without_req_rows_and_strided_q():
+    banner("decode identity rows + strided q")
+    inp = small_decode(60, 32, 8, [100, 300, 2], num_slots=2048)
+    # table rows in request order; q as a view into a wider buffer
+    pt = np.stack([inp.page_table[r] for r in inp.dec_req_rows] + [inp.page_table[-1]])
+    u = Uploaded(inp)
+    u.store()
+    wide = torch.zeros((3, 48, 128), dtype=torch.bfloat16, device="cuda")
+    wide[:, 8:40] = u.dq
+    q = wide[:, 8:40]
+    out, lse = msgl.paged_decode(q, u.k, u.v, up(pt.astype(np.int32)), u.d_lens, u.d_max,
+                                 inp.sm_scale, split_tokens=64)
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle_decode(inp, kp, vp)
+    assert_close(out, ro, "identity rows")
+
+
+def test_decode_seq_len_one_is_the_value_row_bit_exact():
+    banner("decode seq_len=1 bitwise")
+    inp = small_decode(61, 32, 8, [1] * 7, num_slots=512)
+    u = Uploaded(inp)
+    u.store()
+    out, lse = u.decode()
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    got = bits(out)
+    for r in range(7):
+        slot = inp.page_table[inp.dec_req_rows[r], 0]
+        for h in range(32):
+            assert np.array_equal(got[r, h], vp[slot, h // 4]), (r, h)
+
+
+def test_decode_slot_permutation_bitwise():
+    banner("decode slot permutation bitwise")
+    inp = small_decode(62, 32, 8, [700, 33, 1200, 64], num_slots=4096)
+    u = Uploaded(inp)
+    u.store()
+    o1, l1 = u.decode(split_tokens=256)
+    pi = np.random.default_rng(9).permutation(inp.num_slots)
+    kp, vp = oracle_pool(inp)
+    k2 = np.empty_like(kp); v2 = np.empty_like(vp)
+    k2[pi] = kp; v2[pi] = vp
+    pt2 = pi[inp.page_table].astype(np.int32)
+    o2, l2 = msgl.paged_decode(u.dq, up(k2), up(v2), up(pt2), u.d_lens, u.d_max, inp.sm_scale,
+                               req_rows=u.d_rows, split_tokens=256)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o1), bits(o2))
+    assert np.array_equal(l1.cpu().numpy(), l2.cpu().numpy())
+
+
+def test_decode_page_size_16_matches_page_size_1_bitwise_and_oracle():
+    banner("decode page_size 16 vs 1")
+    inp = small_decode(63, 32, 8, [1000, 17, 512, 300], page_size=16, num_slots=8192,
+                       shared_prefix=16, shared_by=(0, 1, 2, 3))
+    u = Uploaded(inp)
+    u.store()
+    o16, l16 = u.decode(page_size=16)
+    o1, l1 = u.decode(page_size=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o16), bits(o1))
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle_decode(inp, kp, vp)
+    assert_close(o16, ro, "page16")
+
+
+def test_decode_is_deterministic():
+    banner("decode determinism")
+    inp = small_decode(64, 64, 8, [3000, 5, 1800], num_slots=8192)
+    u = Uploaded(inp)
+    u.store()
+    outs = [bits(u.decode()[0]) for _ in range(3)]
+    assert all(np.array_equal(outs[0], o) for o in outs[1:])
+
+
+def test_decode_empty_request():
+    banner("decode empty request")
+    inp = small_decode(65, 16, 8, [40, 1, 70], num_slots=1024)
+    u = Uploaded(inp)
+    u.store()
+    lens = inp.dec_seq_lens.copy()
+    lens[1] = 0
+    out, lse = msgl.paged_decode(u.dq, u.k, u.v, u.pt, up(lens), u.d_max, inp.sm_scale,
+                                 req_rows=u.d_rows, split_tokens=32)
+    torch.cuda.synchronize()
+    assert np.all(f64(out)[1] == 0) and np.all(np.isneginf(lse.cpu().numpy()[1]))
+    kp, vp = oracle_pool(inp)
+    ro, _ = oracle.paged_decode(inp.dec_q, kp, vp, inp.page_table, inp.dec_req_rows, lens,
+                                inp.sm_scale, inp.num_kv_heads)
+    assert_close(out, ro, "empty request batch")
+
+
+def test_decode_zero_scale_is_mean_of_values():
+    banner("decode sm_scale=0")
+    inp = small_decode(66, 32, 8, [100, 37], num_slots=1024, sm_scale=0.0)
+    u = Uploaded(inp)
+    u.store()
+    out, lse = u.decode(split_tokens=32)
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    for r in range(2):
+        L = inp.dec_seq_lens[r]
+        slots = inp.page_table[inp.dec_req_rows[r], :L]
+        want = oracle.bf16_to_f64(vp[slots]).mean(axis=0)           # [Hkv, D]
+        ref = np.repeat(want, 4, axis=0)
+        assert_close(out[r], ref, f"mean r={r}")
+        assert np.allclose(lse.cpu().numpy()[r], math.log(L), atol=1e-5)
+
+
+# ---------------------------------------------------------------------------
+# merge
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("parts", [1, 2, 7])
+def test_merge_states_parity(parts):
+    banner(f"merge parts={parts}")
+    rng = np.random.default_rng(parts)
+    N, H, D = 9, 16, 128
+    po = rng.standard_normal((parts, N, H, D)).astype(np.float32)
+    pl = (rng.standard_normal((parts, N, H)) * 3).astype(np.float32)
+    if parts > 1:
+        pl[0, 2, :] = -np.inf               # an empty part
+        pl[:, 3, 5] = -np.inf               # an all-empty (row, head)
+    out, lse = msgl.merge_states(up(po), up(pl), out_dtype=torch.float32)
+    outb, _ = msgl.merge_states(up(po), up(pl), out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ro, rl = oracle.merge_states(po.astype(np.float64), pl.astype(np.float64))
+    assert np.allclose(out.cpu().numpy(), ro, atol=1e-5, rtol=1e-5)
+    assert_close(outb, ro, "merge bf16")
+    got_l = lse.cpu().numpy()
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(got_l), fin)
+    assert np.allclose(got_l[fin], rl[fin], atol=1e-5)
+    if parts > 1:
+        assert np.all(out.cpu().numpy()[3, 5] == 0)
+
+
+# ---------------------------------------------------------------------------
+# extend
+# ---------------------------------------------------------------------------
+
+EXTEND_CASES = [
+    # (hq, hkv, specs)
+    (32, 8, [(0, 1), (0, 33), (7, 64), (100, 65)]),
+    (32, 8, [(300, 200), (0, 129), (64, 31)]),
+    (8, 8, [(50, 130)]),
+    (16, 8, [(0, 257), (1, 3)]),
+    (64, 8, [(200, 40), (0, 77)]),
+    (16, 1, [(90, 70)]),
+]
+
+
+@pytest.mark.parametrize("case", range(len(EXTEND_CASES)))
+def test_extend_parity(case):
+    hq, hkv, specs = EXTEND_CASES[case]
+    banner(f"extend hq={hq} hkv={hkv} specs={specs}")
+    inp = small_extend(80 + case, hq, hkv, specs, num_slots=4096)
+    u = Uploaded(inp)
+    u.store()
+    out, lse = u.extend()
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle_extend(inp, kp, vp)
+    assert_close(out, ro, f"extend case {case}")
+    assert_lse_close(lse, rl, f"extend case {case}")
+
+
+def test_extend_with_shared_prefix_and_page_size_16():
+    banner("extend shared prefix, page 16 vs 1")
+    inp = small_extend(90, 32, 8, [(64, 100), (64, 37), (128, 64)], page_size=16,
+                       num_slots=8192, shared_prefix=64, shared_by=(0, 1, 2))
+    u = Uploaded(inp)
+    u.store()
+    o16, _ = u.extend(page_size=16)
+    o1, _ = u.extend(page_size=1)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o16), bits(o1))
+    kp, vp = oracle_pool(inp)
+    ro, _ = oracle_extend(inp, kp, vp)
+    assert_close(o16, ro, "extend page16")
+
+
+def test_extend_of_one_token_equals_decode():
+    banner("extend(E=1) vs decode")
+    inp = small_decode(91, 32, 8, [500, 1, 64, 1300], num_slots=4096)
+    u = Uploaded(inp)
+    u.store()
+    od, ld = u.decode(split_tokens=4096)
+    L = inp.dec_seq_lens
+    oe, le = msgl.paged_extend(u.dq, u.k, u.v, u.pt, up((L - 1).astype(np.int32)),
+                               up(np.ones_like(L)), up(np.arange(len(L) + 1, dtype=np.int32)),
+                               1, int(L.max()), inp.sm_scale, req_rows=u.d_rows)
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    ro, _ = oracle_decode(inp, kp, vp)
+    assert_close(oe, ro, "extend E=1")
+    assert np.abs(f64(oe) - f64(od)).max() <= 2e-2
+
+
+def test_extend_chunked_equals_full_prefill():
+    banner("extend chunked vs full")
+    N = 300
+    inp = small_extend(92, 32, 8, [(0, N)], num_slots=2048)
+    u = Uploaded(inp)
+    u.store()
+    full, _ = u.extend()
+    row = inp.page_table[inp.ext_req_rows[0]][None, :]
+    cuts = [0, 100, 229, N]
+    kp, vp = oracle_pool(inp)
+    ro, _ = oracle_extend(inp, kp, vp)
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        oc, _ = msgl.paged_extend(u.eq[a:b].contiguous(), u.k, u.v, up(row.astype(np.int32)),
+                                  up(np.array([a], np.int32)), up(np.array([b - a], np.int32)),
+                                  up(np.array([0, b - a], np.int32)), b - a, b, inp.sm_scale)
+        torch.cuda.synchronize()
+        assert_close(oc, ro[a:b], f"chunk {a}:{b}")
+        assert np.abs(f64(oc) - f64(full[a:b])).max() <= 2e-2
