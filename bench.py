@@ -1,0 +1,359 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+A step is one pass of the path over one synthetic batch with every input
+already resident in HBM.  The headline workload is the 8B-class decode
+batch (Hq 32 / Hkv 8 / head_dim 128, 64 requests with kv lengths uniform
+in [512, 4096], a 512K-slot randomly permuted pool, page_size 1): a step is
+``store_kv`` of the 64 new K/V rows followed by the split-KV paged decode
+(decode kernel + LSE merge).  The line also carries the extend workload
+(8 chunked-prefill requests over prefixes up to 8K, 4 of them sharing one
+2,048-slot prefix) and, with ``--configs``, the long-tail and mixed-batch
+workloads.
+
+Prints ONE JSON line (rank 0, N = 1).  ``value`` = distinct K/V bytes the
+decode must read / (wall time of the K timed steps / K).
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "paged decode KV GB/s + extend TFLOP/s on 1 MI355X, % of roofline"
+KERNEL_SOURCES = ["decode.hip", "merge.hip", "common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c2_traffic.json")
+
+WORKLOAD_TEXT = {
+    "C2": "paged GQA decode + store_kv: Hq 32 / Hkv 8 / D 128, batch 64, kv lens U[512,4096], "
+          "524,288-slot randomly permuted pool, page_size 1, bf16 N(0,1), seed 2",
+    "C3": "causal chunked-prefill extend + store_kv: Hq 32 / Hkv 8 / D 128, batch 8, prefixes "
+          "[2048 x4 shared, 0, 1024, 4096, 8192], extend lens U[512,2048], page_size 1, seed 3",
+    "C4": "long-tail paged decode + store_kv: Hq 64 / Hkv 8 / D 128, batch 256, kv lens "
+          "lognormal(median 2048, sigma 1) clipped to [1024, 32768], split-KV + LSE merge, seed 4",
+    "C5a": "mixed batch, page_size 1: store_kv of 2,175 rows + decode of 127 requests "
+           "(lens U[256,8192]) + extend (prefix 6144, extend 2048); 64 requests share a "
+           "1,024-token prefix; Hq 32 / Hkv 8, seed 5",
+    "C5b": "mixed batch as C5a at page_size 16 (16-slot pages, page permutation), seed 5",
+}
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_attention_30_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def upload(inp):
+    """Copy one synthetic batch to the GPU (bf16 tensors keep their bits)."""
+    import torch
+
+    def up(a):
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if a.dtype == np.uint16:
+            x = x.view(torch.int16).view(torch.bfloat16)
+        return x.to("cuda")
+    t = {"k": up(inp.k_pool), "v": up(inp.v_pool), "pt": up(inp.page_table),
+         "out_loc": up(inp.out_loc), "k_new": up(inp.k_new), "v_new": up(inp.v_new)}
+    if inp.num_decode:
+        t.update(dq=up(inp.dec_q), d_rows=up(inp.dec_req_rows), d_lens=up(inp.dec_seq_lens),
+                 d_max=int(inp.dec_seq_lens.max()))
+    if inp.num_extend:
+        t.update(eq=up(inp.ext_q), e_rows=up(inp.ext_req_rows), e_pre=up(inp.ext_prefix_lens),
+                 e_ext=up(inp.ext_extend_lens), e_off=up(inp.ext_q_offsets),
+                 e_max=int(inp.ext_extend_lens.max()),
+                 e_kv=int((inp.ext_prefix_lens + inp.ext_extend_lens).max()))
+    return t
+
+
+class Run:
+    """One workload on the GPU: uploads once, then enqueues steps."""
+
+    def __init__(self, inp, split_tokens: int = 0):
+        import torch
+        import paged_kv_attention_30_amd as msgl
+        self.torch, self.msgl, self.inp = torch, msgl, inp
+        self.t = upload(inp)
+        self.split = split_tokens
+        t = self.t
+        self.dec_out = self.dec_lse = self.ws = None
+        if inp.num_decode:
+            B, hq = inp.num_decode, inp.num_q_heads
+            self.dec_out = torch.empty((B, hq, 128), dtype=torch.bfloat16, device="cuda")
+            self.dec_lse = torch.empty((B, hq), dtype=torch.float32, device="cuda")
+            need, self.split_used = msgl.paged_decode_workspace_size(
+                B, hq, inp.num_kv_heads, t["d_max"], split_tokens)
+            self.ws = msgl.alloc_workspace(need)
+        if inp.num_extend:
+            T = inp.ext_tokens
+            self.ext_out = torch.empty((T, inp.num_q_heads, 128), dtype=torch.bfloat16, device="cuda")
+            self.ext_lse = torch.empty((T, inp.num_q_heads), dtype=torch.float32, device="cuda")
+
+    def store(self):
+        t = self.t
+        self.msgl.store_kv(t["k"], t["v"], t["k_new"], t["v_new"], t["out_loc"])
+
+    def decode(self):
+        t, inp = self.t, self.inp
+        self.msgl.paged_decode(t["dq"], t["k"], t["v"], t["pt"], t["d_lens"], t["d_max"],
+                               inp.sm_scale, req_rows=t["d_rows"], page_size=inp.page_size,
+                               split_tokens=self.split, out=self.dec_out, lse=self.dec_lse,
+                               workspace=self.ws)
+
+    def extend(self):
+        t, inp = self.t, self.inp
+        self.msgl.paged_extend(t["eq"], t["k"], t["v"], t["pt"], t["e_pre"], t["e_ext"],
+                               t["e_off"], t["e_max"], t["e_kv"], inp.sm_scale,
+                               req_rows=t["e_rows"], page_size=inp.page_size, out=self.ext_out,
+                               lse=self.ext_lse)
+
+    def step(self):
+        self.store()
+        if self.inp.num_decode:
+            self.decode()
+        if self.inp.num_extend:
+            self.extend()
+
+
+def timed_steps(run: Run, steps: int, warmup: int):
+    """Warm up, then time exactly ``steps`` steps; per-phase HIP events inside."""
+    torch = run.torch
+    for _ in range(warmup):
+        run.step()
+    torch.cuda.synchronize()
+    evs = []
+    t0 = time.perf_counter()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        run.store()
+        e[1].record()
+        if run.inp.num_decode:
+            run.decode()
+        e[2].record()
+        if run.inp.num_extend:
+            run.extend()
+        e[3].record()
+        evs.append(e)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    store_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    ext_ms = [e[2].elapsed_time(e[3]) for e in evs]
+    return dict(total_ms=total_ms, wall_s=wall, store_ms=store_ms, dec_ms=dec_ms, ext_ms=ext_ms)
+
+
+def cold_decode_ms(run: Run, reps: int = 10):
+    """Decode time with L2 and the 256 MB Infinity Cache flushed before each call."""
+    torch = run.torch
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    out = []
+    for _ in range(reps):
+        scratch.add_(1)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        run.decode()
+        b.record()
+        torch.cuda.synchronize()
+        out.append(a.elapsed_time(b))
+    del scratch
+    return float(np.median(out))
+
+
+def load_traffic(khash: str, launches_bytes: float):
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        d = json.load(f)
+    if d.get("kernel_hash") != khash:
+        return None
+    return d.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s: float = 15.0):
+    """Time the oracle on a bounded sample of the decode workload (rank 0)."""
+    import oracle
+    from workloads import metrics
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    try:
+        kp, vp = oracle.store_kv(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.out_loc)
+        done = 0
+        t0 = time.perf_counter()
+        kv_bytes = 0
+        while done < inp.num_decode and time.perf_counter() - t0 < budget_s:
+            sel = slice(done, done + 1)
+            oracle.paged_decode(inp.dec_q[sel], kp, vp, inp.page_table, inp.dec_req_rows[sel],
+                                inp.dec_seq_lens[sel], inp.sm_scale, inp.num_kv_heads)
+            kv_bytes += metrics.decode_kv_bytes(inp.page_table, inp.dec_req_rows[sel],
+                                                inp.dec_seq_lens[sel], inp.num_kv_heads, 128)
+            done += 1
+        dt = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"fp64 numpy oracle decode of the first {done} of {inp.num_decode} requests "
+                      f"of the headline batch ({kv_bytes / 1e6:.1f} MB distinct K/V) in {dt:.1f} s, "
+                      f"BLAS limited to 1 thread; host {platform.processor() or platform.machine()}, "
+                      f"{os.cpu_count()} logical CPUs visible"}
+
+
+def decode_figures(inp, res, steps):
+    from workloads import metrics
+    kv = metrics.decode_kv_bytes(inp.page_table, inp.dec_req_rows, inp.dec_seq_lens,
+                                 inp.num_kv_heads, 128)
+    alg = metrics.decode_bytes(inp.page_table, inp.dec_req_rows, inp.dec_seq_lens,
+                               inp.num_q_heads, inp.num_kv_heads, 128)
+    dec_ms = float(np.mean(res["dec_ms"]))
+    return kv, alg, dec_ms
+
+
+def extend_figures(inp, res):
+    from workloads import metrics
+    fl = metrics.extend_flops(inp.ext_prefix_lens, inp.ext_extend_lens, inp.num_q_heads, 128)
+    ext_ms = float(np.mean(res["ext_ms"]))
+    return fl, ext_ms
+
+
+def summarize(name, inp, run, res, steps):
+    d = {"workload": WORKLOAD_TEXT.get(name, name)}
+    step_ms = res["total_ms"] / steps
+    d["ms_per_step"] = round(step_ms, 4)
+    d["store_ms"] = round(float(np.mean(res["store_ms"])), 4)
+    if inp.num_decode:
+        kv, alg, dec_ms = decode_figures(inp, res, steps)
+        d["decode_ms"] = round(dec_ms, 4)
+        d["decode_kv_gb"] = round(kv / 1e9, 4)
+        d["decode_kv_GBps"] = round(kv / (dec_ms * 1e-3) / 1e9, 1)
+        d["decode_alg_GBps"] = round(alg / (dec_ms * 1e-3) / 1e9, 1)
+        d["decode_hbm_frac"] = round(alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        d["decode_tokens_per_s"] = round(inp.num_decode / (dec_ms * 1e-3), 1)
+        d["decode_split_tokens"] = run.split_used
+    if inp.num_extend:
+        fl, ext_ms = extend_figures(inp, res)
+        d["extend_ms"] = round(ext_ms, 4)
+        d["extend_tflops"] = round(fl / (ext_ms * 1e-3) / 1e12, 2)
+        d["extend_mfma_frac"] = round(fl / (ext_ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)
+        d["extend_tokens_per_s"] = round(inp.ext_tokens / (ext_ms * 1e-3), 1)
+    return d
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--configs", default="C3", help="extra workloads (comma list of C3,C4,C5a,C5b; '' for none)")
+    ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cold", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the attention shards by request or kv head with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import paged_kv_attention_30_amd as msgl
+    from workloads import make_config
+
+    msgl.load()
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+
+    log("generating the headline decode batch")
+    inp = make_config("C2")
+    run = Run(inp, args.split_tokens)
+    log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
+    res = timed_steps(run, args.steps, args.warmup)
+    head = summarize("C2", inp, run, res, args.steps)
+    kv, alg, dec_ms = decode_figures(inp, res, args.steps)
+    step_s = res["total_ms"] * 1e-3 / args.steps
+    value = kv / step_s / 1e9
+    if not args.no_cold:
+        head["decode_ms_cold_l2_mall_flushed"] = round(cold_decode_ms(run), 4)
+
+    khash = kernel_hash()
+    traffic = load_traffic(khash, alg)
+    roofline = {"bound": "hbm", "achieved": round(alg / (dec_ms * 1e-3) / 1e9, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "traffic": traffic,
+                "kernel": "paged_decode_kernel<8> + merge_kernel (one msgl_paged_decode call)",
+                "alg_bytes_per_launch": alg, "avg_launch_ms": round(dec_ms, 4)}
+    del run
+    torch.cuda.empty_cache()
+
+    extras = {"C2": head}
+    for name in [c for c in args.configs.split(",") if c]:
+        log(f"workload {name}")
+        inp_x = make_config(name)
+        run_x = Run(inp_x, args.split_tokens)
+        res_x = timed_steps(run_x, max(5, args.steps // 5), 3)
+        extras[name] = summarize(name, inp_x, run_x, res_x, max(5, args.steps // 5))
+        del run_x
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(inp)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["total_ms"] / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_TEXT["C2"], "step": "store_kv(64 rows) + paged_decode (+LSE merge)",
+                   "split_tokens": head.get("decode_split_tokens"), "page_size": 1},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "extras": extras,
+        "kernel_hash": khash,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

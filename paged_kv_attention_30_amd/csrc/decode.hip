@@ -179,10 +179,12 @@ paged_decode_kernel(DecodeParams p) {
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const uint32_t lo = f32_to_bf16_rne(fast_exp2(sv[2 * e] - m_new));
-      const uint32_t hi = f32_to_bf16_rne(fast_exp2(sv[2 * e + 1] - m_new));
-      pw[e] = lo | (hi << 16);
-      psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
+      // the running sum takes the fp32 weights (an exact lse); the PV
+      // contraction takes them rounded to bf16
+      const float p0 = fast_exp2(sv[2 * e] - m_new);
+      const float p1 = fast_exp2(sv[2 * e + 1] - m_new);
+      pw[e] = pack_bf16x2(p0, p1);
+      psum += p0 + p1;
     }
     l_run = l_run * alpha + psum;
     const u32x4 pb = {pw[0], pw[1], pw[2], pw[3]};

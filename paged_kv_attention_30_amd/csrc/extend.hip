@@ -197,10 +197,10 @@ paged_extend_kernel(ExtendParams p) {
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const int i0 = 8 * (u & 1) + 2 * e2;
-        const uint32_t lo = f32_to_bf16_rne(fast_exp2(s[u >> 1][i0] - m_new));
-        const uint32_t hi = f32_to_bf16_rne(fast_exp2(s[u >> 1][i0 + 1] - m_new));
-        pb[u][e2] = lo | (hi << 16);
-        psum += __uint_as_float(lo << 16) + __uint_as_float(hi << 16);
+        const float p0 = fast_exp2(s[u >> 1][i0] - m_new);
+        const float p1 = fast_exp2(s[u >> 1][i0 + 1] - m_new);
+        pb[u][e2] = pack_bf16x2(p0, p1);
+        psum += p0 + p1;
       }
     }
     l_run = l_run * alpha + psum;
