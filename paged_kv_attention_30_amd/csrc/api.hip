@@ -36,7 +36,6 @@ int fail(int status, const char* file, int line, const char* fmt, ...) {
   } while (0)
 
 constexpr int kHeadDim = 128;
-constexpr int kDefaultSplit = 256;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
@@ -51,15 +50,45 @@ int launch_status(hipError_t e, const char* what) {
   return MSGL_FAIL(MSGL_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
 }
 
-// Split size: keep at least ~4 chunks of work per compute unit when the
-// batch is small, never below 64 keys; the value depends on host sizes only.
-int32_t resolve_split(int32_t batch, int32_t num_kv_heads, int32_t max_seq_len,
-                      int32_t requested) {
-  if (requested > 0) return requested;
-  (void)num_kv_heads;
-  (void)batch;
-  (void)max_seq_len;
-  return kDefaultSplit;
+// Compute units of the current device (cached per device).
+int device_compute_units() {
+  static int cu_cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  int cus = cu_cache[dev];
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cu_cache[dev] = cus;
+  }
+  return cus;
+}
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Workspace layout of one decode call: partial outputs, partial lse, and
+// (balanced mode) the per-request workgroup ranges.
+struct DecodeWorkspace {
+  size_t part_out_bytes, part_lse_bytes, meta_bytes;
+  size_t total() const { return part_out_bytes + part_lse_bytes + meta_bytes; }
+};
+
+DecodeWorkspace decode_workspace(int32_t batch, int32_t num_q_heads, int32_t head_dim,
+                                 int32_t max_seq_len, int32_t split_tokens) {
+  DecodeWorkspace w{0, 0, 0};
+  int64_t rows;
+  if (split_tokens > 0) {
+    const int64_t splits = ((int64_t)max_seq_len + split_tokens - 1) / split_tokens;
+    if (splits <= 1) return w;
+    rows = splits * batch;
+  } else {
+    rows = (int64_t)msgl::kMaxDecodeBlocks + batch;
+    w.meta_bytes = align256((size_t)batch * 2 * sizeof(int32_t));
+  }
+  w.part_out_bytes = align256((size_t)rows * num_q_heads * head_dim * sizeof(float));
+  w.part_lse_bytes = align256((size_t)rows * num_q_heads * sizeof(float));
+  return w;
 }
 
 int validate_pool(const void* k_cache, const void* v_cache, int64_t num_slots,
@@ -153,19 +182,11 @@ int msgl_store_kv(void* k_cache, void* v_cache, int64_t num_slots, int64_t cache
 size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t max_seq_len,
                                         int32_t split_tokens, int32_t* split_tokens_out) {
-  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len <= 0) {
-    if (split_tokens_out) *split_tokens_out = 0;
+  (void)num_kv_heads;
+  if (split_tokens_out) *split_tokens_out = split_tokens > 0 ? split_tokens : 0;
+  if (batch <= 0 || num_q_heads <= 0 || head_dim <= 0 || max_seq_len < 0 || split_tokens < 0)
     return 0;
-  }
-  const int32_t S = resolve_split(batch, num_kv_heads, max_seq_len, split_tokens);
-  if (split_tokens_out) *split_tokens_out = S;
-  const int64_t splits = ((int64_t)max_seq_len + S - 1) / S;
-  if (splits <= 1) return 0;
-  const int64_t rows = splits * batch * num_q_heads;
-  size_t bytes = (size_t)rows * head_dim * sizeof(float);
-  bytes = (bytes + 255) / 256 * 256;
-  bytes += (size_t)rows * sizeof(float);
-  return (bytes + 255) / 256 * 256;
+  return decode_workspace(batch, num_q_heads, head_dim, max_seq_len, split_tokens).total();
 }
 
 int msgl_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_stride,
@@ -200,10 +221,9 @@ int msgl_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_st
                  (!lse_out || aligned(lse_out, 4)),
              MSGL_ERR_ALIGN, "int32/fp32 arrays must be 4-byte aligned");
 
-  int32_t S = 0;
-  const size_t need = msgl_paged_decode_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
-                                                       max_seq_len > 0 ? max_seq_len : 1,
-                                                       split_tokens, &S);
+  const DecodeWorkspace ws = decode_workspace(batch, num_q_heads, head_dim, max_seq_len,
+                                              split_tokens);
+  const size_t need = ws.total();
   MSGL_CHECK(workspace_bytes >= need, MSGL_ERR_WORKSPACE, "workspace %zu bytes < required %zu",
              workspace_bytes, need);
   MSGL_CHECK(need == 0 || (workspace && aligned(workspace, 256)), MSGL_ERR_WORKSPACE,
@@ -228,13 +248,18 @@ int msgl_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_st
   a.max_seq_len = max_seq_len;
   a.sm_scale = sm_scale;
   a.stream = stream;
-  a.split_tokens = S;
-  a.max_splits = max_seq_len > 0 ? (int32_t)(((int64_t)max_seq_len + S - 1) / S) : 1;
-  const int64_t rows = (int64_t)a.max_splits * batch * num_q_heads;
+  a.split_tokens = split_tokens;
   a.part_out = need ? (float*)workspace : nullptr;
-  a.part_lse = need ? (float*)((char*)workspace + ((size_t)rows * head_dim * 4 + 255) / 256 * 256)
-                    : nullptr;
-  if (!need) a.max_splits = 1;
+  a.part_lse = need ? (float*)((char*)workspace + ws.part_out_bytes) : nullptr;
+  a.meta = ws.meta_bytes ? (int32_t*)((char*)workspace + ws.part_out_bytes + ws.part_lse_bytes)
+                         : nullptr;
+  if (split_tokens > 0) {
+    a.balanced_blocks = 0;
+    a.max_splits = need ? (int32_t)(((int64_t)max_seq_len + split_tokens - 1) / split_tokens) : 1;
+  } else {
+    a.balanced_blocks = device_compute_units();
+    a.max_splits = 0;
+  }
   return launch_status(msgl::launch_paged_decode(a), "paged_decode");
 }
 
@@ -336,6 +361,7 @@ int msgl_merge_states(void* out, float* lse_out, const float* part_out, const fl
   a.out_bf16 = out_dtype == MSGL_DTYPE_BF16;
   a.seq_lens = nullptr;
   a.split_tokens = 0;
+  a.meta = nullptr;
   a.stream = stream;
   return launch_status(msgl::launch_merge(a), "merge_states");
 }

@@ -8,7 +8,19 @@
 // view), so key j of a request sits in slot page_table[row, j]; §4.6.7 — the
 // new token was stored before the kernel runs, so seq_len counts it.
 //
-// gfx950 design (one wave = one kv head of one request over one key chunk):
+// gfx950 design.  A workgroup has one wave per kv head (up to 8) and walks
+// one range of keys; all its waves read the same tokens, so every gathered
+// K/V row (num_kv_heads x 256 B) is fetched by one workgroup at one time.
+// * Work split ("balanced" mode, split_tokens = 0): the keys of the whole
+//   batch, laid end to end in request order, are cut into gridDim.x equal
+//   ranges, one per workgroup; the grid is sized to the number of
+//   workgroups the GPU holds at once, so the whole batch runs in a single
+//   round with equal work everywhere.  A range may cover the tail of one
+//   request, several whole requests and the head of another; a request
+//   covered by one workgroup is finished there, a request cut across
+//   workgroups leaves normalised fp32 partials + lse that the merge kernel
+//   combines.  ("Fixed" mode, split_tokens = S > 0: chunk c of request r is
+//   keys [cS, (c+1)S), one workgroup per (chunk, request).)
 // * Keys are processed 32 at a time.  Each lane fetches the page-table entry
 //   of "its" token and issues 16-byte loads of that token's K and V row
 //   segment (a wave reads 64 contiguous bytes per token per instruction).
@@ -20,11 +32,9 @@
 // * O^T = V^T P^T also runs on MFMA: P^T is the QK output repacked to bf16
 //   in place (its C layout is exactly the B layout of the next MFMA), and V^T
 //   is staged through a wave-private LDS tile written transposed.
-// * Split-KV: chunk c of request r covers keys [c*S, (c+1)*S).  Requests with
-//   one chunk write the final bf16 output; the others write normalised fp32
-//   partials + lse that msgl_merge_states' kernel combines.
-// * Reduction order depends only on logical key positions, so results are
-//   bit-identical under any slot permutation and for any page_size.
+// * Reduction order depends only on logical key positions and lengths, so
+//   results are bit-identical under any slot permutation and for any
+//   page_size.
 
 #include <float.h>
 
@@ -53,11 +63,12 @@ struct DecodeParams {
   int32_t batch;
   int32_t num_q_heads;
   int32_t ratio;
-  int32_t split_tokens;
-  int32_t max_splits;
+  int32_t split_tokens;   // fixed mode chunk size (> 0), 0 in balanced mode
+  int32_t max_splits;     // fixed mode: chunks per request in the grid
   float scale_log2;       // sm_scale * log2(e)
-  float* part_out;
-  float* part_lse;
+  float* part_out;        // [slots, Hq, 128]
+  float* part_lse;        // [slots, Hq]
+  int32_t* meta;          // balanced mode: per request (first, last) workgroup
 };
 
 // position of key t (0..31 of a tile) inside a V^T row: the B-operand slot
@@ -67,63 +78,71 @@ __device__ __forceinline__ int vt_pos(int t) {
   return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3);
 }
 
-template <int KVB>
-__global__ void __launch_bounds__(KVB * 64)
-paged_decode_kernel(DecodeParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[KVB][kHeadDim * kVtPitch];
+__device__ __forceinline__ int shfl_up_i(int v, int d) {
+  const int lane = __lane_id();
+  const int src = lane >= d ? lane - d : lane;
+  return __builtin_amdgcn_ds_bpermute(src << 2, v);
+}
 
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int r = blockIdx.x % p.batch;
-  const int split = blockIdx.x / p.batch;
-  const int g = blockIdx.y * KVB + w;
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = __lane_id();
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int t = shfl_up_i(v, d);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// A value every lane holds identically, moved to scalar registers.
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const int lo = __builtin_amdgcn_readfirstlane((int)(uint32_t)(v & 0xffffffff));
+  const int hi = __builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+  return ((int64_t)hi << 32) | (uint32_t)lo;
+}
+
+// Output of an empty request: zeros and lse = -inf.
+__device__ __forceinline__ void write_empty(const DecodeParams& p, int r, int g, int c, int j) {
+  if (c >= p.ratio) return;
+  const int h = g * p.ratio + c;
+  uint16_t* o = p.out + ((int64_t)r * p.num_q_heads + h) * kHeadDim;
+  const u32x2 z = {0u, 0u};
+#pragma unroll
+  for (int mb = 0; mb < 8; ++mb) *reinterpret_cast<u32x2*>(o + 16 * mb + 4 * j) = z;
+  if (p.lse && j == 0) p.lse[(int64_t)r * p.num_q_heads + h] = -INFINITY;
+}
+
+// One wave: attention of request r's q heads of kv head g over keys
+// [t0, t1) (t0 < t1).  Writes the final bf16 output + lse when `whole`,
+// else the normalised fp32 partial + lse at partial row `slot`.
+// `vt` is the wave's V^T tile (128 x kVtPitch), `qs` its q rows (ratio x 128).
+__device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* vt,
+                                               uint16_t* qs, int r, int g, int t0, int t1,
+                                               bool whole, int64_t slot) {
+  const int lane = __lane_id();
   const int c = lane & 15;      // q-head column / token row inside the MFMA
   const int j = lane >> 4;      // k-slot group
   const int R = p.ratio;
-  const int S = p.split_tokens;
-
-  const int L = p.seq_lens[r];
-  const int t0 = split * S;
-  // a length beyond the host bound folds its tail into the last chunk, so
-  // no chunk index ever exceeds the workspace
-  const int nsplit = min((L + S - 1) / S, p.max_splits);
-
-  if (L <= 0) {
-    // empty request: output 0, lse -inf (written once, by chunk 0)
-    if (split == 0 && c < R) {
-      const int h = g * R + c;
-      uint16_t* o = p.out + ((int64_t)r * p.num_q_heads + h) * kHeadDim;
-      for (int mb = 0; mb < 8; ++mb) {
-        u32x2 z = {0u, 0u};
-        *reinterpret_cast<u32x2*>(o + 16 * mb + 4 * j) = z;
-      }
-      if (p.lse && j == 0) p.lse[(int64_t)r * p.num_q_heads + h] = -INFINITY;
-    }
-    return;
-  }
-  if (t0 >= L) return;
-  const int t1 = (split == p.max_splits - 1) ? L : min(t0 + S, L);
 
   const int row = p.req_rows ? p.req_rows[r] : r;
   const int32_t* pt = p.page_table + (int64_t)row * p.pt_stride;
 
-  // q of this lane's head as the B operand of S^T = K Q^T:
-  // column c, k-slot (j, e) of step kk <-> head dim 32*kk + 8*j + e.
-  u32x4 qb[4];
+  // q rows of the group into LDS (ratio x 128 bf16, 16 bytes per lane step)
   {
-    const bool valid = c < R;
-    const uint16_t* qrow = p.q + (int64_t)r * p.q_stride + (int64_t)(g * R + (valid ? c : 0)) * kHeadDim;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u32x4 v = ld16(qrow + 32 * kk + 8 * j);
-      qb[kk] = valid ? v : u32x4{0u, 0u, 0u, 0u};
-    }
+    const uint16_t* qg = p.q + (int64_t)r * p.q_stride + (int64_t)g * R * kHeadDim;
+    __builtin_amdgcn_wave_barrier();
+    for (int u = lane; u < R * 16; u += 64)
+      *reinterpret_cast<u32x4*>(qs + 8 * u) = ld16(qg + 8 * u);
+    __builtin_amdgcn_wave_barrier();
   }
+  // B operand of S^T = K Q^T: column c, k-slot (j, e) of step kk <-> head dim
+  // 32*kk + 8*j + e.  Columns c >= ratio read a real row again; their output
+  // columns are never used and MFMA columns do not mix.
+  const uint16_t* qcol = qs + (c % R) * kHeadDim + 8 * j;
 
   const int64_t cs = p.cache_stride_bytes;
-  const char* kbase = p.k_cache + (int64_t)g * kHeadDim * 2 + (32 * 0 + 8 * j) * 2;
-  const char* vbase = p.v_cache + (int64_t)g * kHeadDim * 2 + (8 * j) * 2;
-  uint16_t* vt = vt_lds[w];
+  const char* kbase = p.k_cache + (int64_t)g * kHeadDim * 2 + (8 * j) * 2;
+  const int64_t v_minus_k = p.v_cache - p.k_cache;   // same layout, other plane
   const int pos_a = vt_pos(c);        // key c of the tile
   const int pos_b = vt_pos(16 + c);   // key 16 + c
 
@@ -133,29 +152,54 @@ paged_decode_kernel(DecodeParams p) {
   float m_run = -INFINITY;   // running max, log2 units
   float l_run = 0.f;         // this lane's share of the running sum
 
-  for (int tb = t0; tb < t1; tb += kTile) {
-    const int ta = min(tb + c, t1 - 1);
-    const int tbb = min(tb + 16 + c, t1 - 1);
-    const int64_t sa = (int64_t)pt[ta];
-    const int64_t sb = (int64_t)pt[tbb];
+  // The page-table entries of tile i+1 are fetched while tile i computes,
+  // so each iteration waits on one memory latency (its K/V), not two.
+  int na = pt[min(t0 + c, t1 - 1)];
+  int nb = pt[min(t0 + 16 + c, t1 - 1)];
 
-    u32x4 ka[4], kb[4], va[4], vb[4];
+  for (int tb = t0; tb < t1; tb += kTile) {
+    const char* ra = kbase + (int64_t)na * cs;
+    const char* rb = kbase + (int64_t)nb * cs;
+    // V first: it goes to LDS as soon as it lands, which frees its
+    // registers before the QK operands are needed
+    u32x4 va[4], vb[4], ka[4], kb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      ka[kk] = ld16(kbase + sa * cs + 64 * kk);
-      kb[kk] = ld16(kbase + sb * cs + 64 * kk);
+      va[kk] = ld16(ra + v_minus_k + 64 * kk);
+      vb[kk] = ld16(rb + v_minus_k + 64 * kk);
     }
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      va[kk] = ld16(vbase + sa * cs + 64 * kk);
-      vb[kk] = ld16(vbase + sb * cs + 64 * kk);
+      ka[kk] = ld16(ra + 64 * kk);
+      kb[kk] = ld16(rb + 64 * kk);
     }
+    if (tb + kTile < t1) {
+      na = pt[min(tb + kTile + c, t1 - 1)];
+      nb = pt[min(tb + kTile + 16 + c, t1 - 1)];
+    }
+
+    // V^T tile: lane holds V[key c][dims 32kk+8j .. +7] and V[key 16+c][...]
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = 32 * kk + 8 * j + 2 * e;
+        const uint32_t wa = va[kk][e];
+        const uint32_t wb = vb[kk][e];
+        vt[d * kVtPitch + pos_a] = (uint16_t)(wa & 0xffffu);
+        vt[(d + 1) * kVtPitch + pos_a] = (uint16_t)(wa >> 16);
+        vt[d * kVtPitch + pos_b] = (uint16_t)(wb & 0xffffu);
+        vt[(d + 1) * kVtPitch + pos_b] = (uint16_t)(wb >> 16);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
 
     f32x4 s_a = {0.f, 0.f, 0.f, 0.f}, s_b = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      s_a = mfma16x16x32(ka[kk], qb[kk], s_a);
-      s_b = mfma16x16x32(kb[kk], qb[kk], s_b);
+      const u32x4 qk = *reinterpret_cast<const u32x4*>(qcol + 32 * kk);
+      s_a = mfma16x16x32(ka[kk], qk, s_a);
+      s_b = mfma16x16x32(kb[kk], qk, s_b);
     }
 
     // lane holds scores of keys tb+4j+i (s_a) and tb+16+4j+i (s_b), head c
@@ -189,23 +233,6 @@ paged_decode_kernel(DecodeParams p) {
     l_run = l_run * alpha + psum;
     const u32x4 pb = {pw[0], pw[1], pw[2], pw[3]};
 
-    // V^T tile: lane holds V[key c][dims 32kk+8j .. +7] and V[key 16+c][...]
-    __builtin_amdgcn_wave_barrier();
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = 32 * kk + 8 * j + 2 * e;
-        const uint32_t wa = va[kk][e];
-        const uint32_t wb = vb[kk][e];
-        vt[d * kVtPitch + pos_a] = (uint16_t)(wa & 0xffffu);
-        vt[(d + 1) * kVtPitch + pos_a] = (uint16_t)(wa >> 16);
-        vt[d * kVtPitch + pos_b] = (uint16_t)(wb & 0xffffu);
-        vt[(d + 1) * kVtPitch + pos_b] = (uint16_t)(wb >> 16);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
       const u32x4 a = *reinterpret_cast<const u32x4*>(vt + (16 * mb + c) * kVtPitch + 8 * j);
@@ -222,7 +249,7 @@ paged_decode_kernel(DecodeParams p) {
   const float inv = 1.f / l_tot;
   const float lse_nat = (m_run + fast_log2(l_tot)) * kLn2;
 
-  if (nsplit == 1) {
+  if (whole) {
     uint16_t* o = p.out + ((int64_t)r * p.num_q_heads + h) * kHeadDim;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
@@ -233,7 +260,7 @@ paged_decode_kernel(DecodeParams p) {
     }
     if (p.lse && j == 0) p.lse[(int64_t)r * p.num_q_heads + h] = lse_nat;
   } else {
-    const int64_t idx = ((int64_t)split * p.batch + r) * p.num_q_heads + h;
+    const int64_t idx = slot * p.num_q_heads + h;
     float* o = p.part_out + idx * kHeadDim;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
@@ -244,14 +271,158 @@ paged_decode_kernel(DecodeParams p) {
   }
 }
 
+// LDS of one wave: its V^T tile, then its q rows.
+__device__ __forceinline__ uint16_t* wave_lds(uint16_t* base, int w, int ratio) {
+  return base + (size_t)w * (kHeadDim * kVtPitch + ratio * kHeadDim);
+}
+
+// Fixed chunks: workgroup (chunk, request) = blockIdx.x.
+template <int KVB>
+__global__ void __launch_bounds__(KVB * 64, 4)
+decode_fixed_kernel(DecodeParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t dyn_lds[];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  uint16_t* vt = wave_lds(dyn_lds, w, p.ratio);
+  uint16_t* qs = vt + kHeadDim * kVtPitch;
+  const int r = blockIdx.x % p.batch;
+  const int split = blockIdx.x / p.batch;
+  const int g = blockIdx.y * KVB + w;
+  const int S = p.split_tokens;
+  const int L = p.seq_lens[r];
+  if (L <= 0) {
+    if (split == 0) write_empty(p, r, g, lane & 15, lane >> 4);
+    return;
+  }
+  const int t0 = split * S;
+  if (t0 >= L) return;
+  // a length beyond the host bound folds its tail into the last chunk, so
+  // no chunk index ever exceeds the workspace
+  const int nsplit = min((L + S - 1) / S, p.max_splits);
+  const int t1 = (split == p.max_splits - 1) ? L : min(t0 + S, L);
+  attend_segment(p, vt, qs, r, g, t0, t1, nsplit == 1, (int64_t)split * p.batch + r);
+}
+
+// Balanced ranges: workgroup b of G owns flattened keys [b*T/G, (b+1)*T/G).
+template <int KVB>
+__global__ void __launch_bounds__(KVB * 64, 4)
+decode_balanced_kernel(DecodeParams p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t dyn_lds[];
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  uint16_t* vt = wave_lds(dyn_lds, w, p.ratio);
+  uint16_t* qs = vt + kHeadDim * kVtPitch;
+  const int g = blockIdx.y * KVB + w;
+  const int b = blockIdx.x;
+  const int Ggrid = gridDim.x;
+  const int B = p.batch;
+
+  // total keys of the batch (every wave computes it; it is tiny)
+  int64_t tl = 0;
+  for (int i = lane; i < B; i += 64) tl += max(p.seq_lens[i], 0);
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const int lo = __builtin_amdgcn_ds_bpermute(((lane ^ d) << 2), (int)(uint32_t)(tl & 0xffffffff));
+    const int hi = __builtin_amdgcn_ds_bpermute(((lane ^ d) << 2), (int)(uint32_t)(tl >> 32));
+    tl += ((int64_t)hi << 32) | (uint32_t)lo;
+  }
+  const int64_t T = uniform64(tl);
+  // with fewer keys than workgroups, only the first T workgroups take keys
+  const int64_t G = min((int64_t)Ggrid, T);
+  const int64_t start = (G > 0 && b < G) ? (int64_t)b * T / G : T;
+  const int64_t end = (G > 0 && b < G) ? (int64_t)(b + 1) * T / G : T;
+  const bool last = (b == Ggrid - 1);
+  if (start == end && !last) return;
+
+  int64_t running = 0;
+  for (int base = 0; base < B; base += 64) {
+    if (running > end || (running == end && !last)) break;
+    const int i = base + lane;
+    const int Li = i < B ? max(p.seq_lens[i], 0) : 0;
+    const int incl = wave_incl_scan(Li);
+    const int64_t c0 = running + (incl - Li);
+    const int64_t c1 = running + incl;
+    bool own;
+    if (i >= B) own = false;
+    else if (Li > 0) own = c1 > start && c0 < end;
+    else own = (c0 >= start && c0 < end) || (last && c0 == T);
+    uint64_t mask = __ballot(own);
+    const int64_t next_running = running + __builtin_amdgcn_readlane(incl, 63);
+    while (mask) {
+      const int bit = __builtin_ctzll(mask);
+      mask &= mask - 1;
+      const int r = base + bit;
+      const int64_t r1 = running + __builtin_amdgcn_readlane(incl, bit);
+      const int64_t r0 = r1 - __builtin_amdgcn_readlane(Li, bit);
+      const bool writer = (w == 0 && blockIdx.y == 0 && lane == 0);
+      if (r1 == r0) {
+        write_empty(p, r, g, lane & 15, lane >> 4);
+        if (writer) {
+          p.meta[2 * r] = -1;
+          p.meta[2 * r + 1] = -1;
+        }
+        continue;
+      }
+      const int s0 = (int)(max(start, r0) - r0);
+      const int s1 = (int)(min(end, r1) - r0);
+      const bool whole = r0 >= start && r1 <= end;
+      attend_segment(p, vt, qs, r, g, s0, s1, whole, (int64_t)b + r);
+      if (writer) {
+        // workgroups holding the first and the last key of request r
+        const int64_t bf = ((r0 + 1) * G - 1) / T;
+        const int64_t bl = (r1 * G - 1) / T;
+        p.meta[2 * r] = whole ? -1 : (int32_t)bf;
+        p.meta[2 * r + 1] = whole ? -1 : (int32_t)bl;
+      }
+    }
+    running = next_running;
+  }
+}
+
+size_t decode_lds_bytes(int kvb, int ratio) {
+  return (size_t)kvb * (kHeadDim * kVtPitch + ratio * kHeadDim) * sizeof(uint16_t);
+}
+
+// Workgroups of the balanced kernel resident per compute unit (cached per
+// device and ratio).
+template <int KVB>
+int resident_blocks_per_cu(int ratio) {
+  static int cached[64][5] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  const int ri = ratio == 1 ? 0 : ratio == 2 ? 1 : ratio == 4 ? 2 : ratio == 8 ? 3 : 4;
+  if (cached[dev][ri] > 0) return cached[dev][ri];
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_balanced_kernel<KVB>, KVB * 64,
+                                                   decode_lds_bytes(KVB, ratio)) != hipSuccess ||
+      n <= 0)
+    n = 1;
+  cached[dev][ri] = n;
+  return n;
+}
+
 template <int KVB>
 hipError_t launch_kvb(const DecodeArgs& a, const DecodeParams& p) {
-  dim3 grid((unsigned)((int64_t)a.max_splits * a.batch), (unsigned)(a.num_kv_heads / KVB));
-  hipLaunchKernelGGL((paged_decode_kernel<KVB>), grid, dim3(KVB * 64), 0, a.stream, p);
+  const unsigned gy = (unsigned)(a.num_kv_heads / KVB);
+  const size_t lds = decode_lds_bytes(KVB, p.ratio);
+  if (a.balanced_blocks > 0) {
+    int64_t g = (int64_t)a.balanced_blocks * resident_blocks_per_cu<KVB>(p.ratio) / gy;
+    if (g < 1) g = 1;
+    if (g > kMaxDecodeBlocks) g = kMaxDecodeBlocks;
+    hipLaunchKernelGGL((decode_balanced_kernel<KVB>), dim3((unsigned)g, gy), dim3(KVB * 64), lds,
+                       a.stream, p);
+  } else {
+    dim3 grid((unsigned)((int64_t)a.max_splits * a.batch), gy);
+    hipLaunchKernelGGL((decode_fixed_kernel<KVB>), grid, dim3(KVB * 64), lds, a.stream, p);
+  }
   return hipGetLastError();
 }
 
 }  // namespace
+
+int decode_kv_heads_per_block(int num_kv_heads) {
+  return num_kv_heads % 8 == 0 ? 8 : num_kv_heads % 4 == 0 ? 4 : num_kv_heads % 2 == 0 ? 2 : 1;
+}
 
 hipError_t launch_paged_decode(const DecodeArgs& a) {
   DecodeParams p;
@@ -274,13 +445,17 @@ hipError_t launch_paged_decode(const DecodeArgs& a) {
   p.scale_log2 = a.sm_scale * kLog2e;
   p.part_out = a.part_out;
   p.part_lse = a.part_lse;
+  p.meta = a.meta;
 
   hipError_t err;
-  if (a.num_kv_heads % 8 == 0) err = launch_kvb<8>(a, p);
-  else if (a.num_kv_heads % 4 == 0) err = launch_kvb<4>(a, p);
-  else if (a.num_kv_heads % 2 == 0) err = launch_kvb<2>(a, p);
-  else err = launch_kvb<1>(a, p);
-  if (err != hipSuccess || a.max_splits <= 1) return err;
+  switch (decode_kv_heads_per_block(a.num_kv_heads)) {
+    case 8: err = launch_kvb<8>(a, p); break;
+    case 4: err = launch_kvb<4>(a, p); break;
+    case 2: err = launch_kvb<2>(a, p); break;
+    default: err = launch_kvb<1>(a, p); break;
+  }
+  if (err != hipSuccess) return err;
+  if (a.balanced_blocks <= 0 && a.max_splits <= 1) return hipSuccess;
 
   MergeArgs m;
   m.out = a.out;
@@ -292,8 +467,9 @@ hipError_t launch_paged_decode(const DecodeArgs& a) {
   m.num_heads = a.num_q_heads;
   m.head_dim = kHeadDim;
   m.out_bf16 = true;
-  m.seq_lens = a.seq_lens;
+  m.seq_lens = a.balanced_blocks > 0 ? nullptr : a.seq_lens;
   m.split_tokens = a.split_tokens;
+  m.meta = a.balanced_blocks > 0 ? a.meta : nullptr;
   m.stream = a.stream;
   return launch_merge(m);
 }

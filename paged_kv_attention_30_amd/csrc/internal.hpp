@@ -46,10 +46,12 @@ struct DecodeArgs {
   int32_t page_size;
   int32_t max_seq_len;
   float sm_scale;
-  int32_t split_tokens;    // resolved (> 0)
-  int32_t max_splits;      // ceil(max_seq_len / split_tokens)
-  float* part_out;         // fp32 [max_splits, B, Hq, 128] (when max_splits > 1)
-  float* part_lse;         // fp32 [max_splits, B, Hq]
+  int32_t split_tokens;    // fixed mode chunk size; 0 in balanced mode
+  int32_t max_splits;      // fixed mode: ceil(max_seq_len / split_tokens)
+  int32_t balanced_blocks; // balanced mode: compute units of the device (0 = fixed mode)
+  float* part_out;         // fp32 [rows, Hq, 128]
+  float* part_lse;         // fp32 [rows, Hq]
+  int32_t* meta;           // balanced mode: int32 [B, 2]
   hipStream_t stream;
 };
 
@@ -87,12 +89,18 @@ struct MergeArgs {
   int32_t num_heads;
   int32_t head_dim;
   bool out_bf16;
-  // decode-internal use: per-row part counts from seq_lens (else num_parts)
+  // decode-internal use: per-row part counts from seq_lens (fixed chunks)
+  // or from (first, last) workgroup pairs (balanced ranges); else num_parts
   const int32_t* seq_lens;
   int32_t split_tokens;
+  const int32_t* meta;
   hipStream_t stream;
 };
 
+// Most workgroups the balanced decode launches along x (sizes its workspace).
+constexpr int kMaxDecodeBlocks = 2048;
+
+int decode_kv_heads_per_block(int num_kv_heads);
 hipError_t launch_store_kv(const StoreArgs& a);
 hipError_t launch_paged_decode(const DecodeArgs& a);
 hipError_t launch_paged_extend(const ExtendArgs& a);

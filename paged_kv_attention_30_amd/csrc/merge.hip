@@ -31,6 +31,7 @@ struct MergeParams {
   int32_t out_bf16;
   const int32_t* seq_lens;
   int32_t split_tokens;
+  const int32_t* meta;
 };
 
 __global__ void __launch_bounds__(256) merge_kernel(MergeParams p) {
@@ -40,27 +41,36 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeParams p) {
   const int h = blockIdx.y * p.heads_per_block + hl;
   if (hl >= p.heads_per_block || h >= p.num_heads) return;
 
+  // part s of this row lives at partial row base + s * step
   int parts = p.num_parts;
+  int64_t base = row, step = p.n;
   if (p.seq_lens) {
     const int L = p.seq_lens[row];
     parts = (L + p.split_tokens - 1) / p.split_tokens;
     if (parts <= 1) return;  // the decode kernel wrote this row itself
     if (parts > p.num_parts) parts = p.num_parts;
+  } else if (p.meta) {
+    const int bf = p.meta[2 * row];
+    const int bl = p.meta[2 * row + 1];
+    if (bf < 0) return;      // finished by a single workgroup
+    parts = bl - bf + 1;
+    base = (int64_t)bf + row;
+    step = 1;
   }
 
-  const int64_t plane = p.n * (int64_t)p.num_heads;
   const int64_t rh = (int64_t)row * p.num_heads + h;
   float M = -INFINITY;
-  for (int s = 0; s < parts; ++s) M = fmaxf(M, p.part_lse[s * plane + rh]);
+  for (int s = 0; s < parts; ++s)
+    M = fmaxf(M, p.part_lse[(base + s * step) * p.num_heads + h]);
 
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
   if (M != -INFINITY) {
     for (int s = 0; s < parts; ++s) {
-      const float ls = p.part_lse[s * plane + rh];
+      const int64_t ph = (base + s * step) * p.num_heads + h;
+      const float ls = p.part_lse[ph];
       const float wgt = fast_exp2((ls - M) * kLog2e);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(
-          p.part_out + (s * plane + rh) * p.head_dim + 4 * d4);
+      const f32x4 v = *reinterpret_cast<const f32x4*>(p.part_out + ph * p.head_dim + 4 * d4);
       acc += v * wgt;
       wsum += wgt;
     }
@@ -98,6 +108,7 @@ hipError_t launch_merge(const MergeArgs& a) {
   p.out_bf16 = a.out_bf16 ? 1 : 0;
   p.seq_lens = a.seq_lens;
   p.split_tokens = a.split_tokens;
+  p.meta = a.meta;
   if (a.n == 0) return hipSuccess;
   dim3 grid((unsigned)a.n, (unsigned)((a.num_heads + p.heads_per_block - 1) / p.heads_per_block));
   hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, a.stream, p);

@@ -91,11 +91,15 @@ def test_decode_empty_batch_is_a_no_op(lib):
 
 
 def test_decode_workspace_size_rule(lib):
+    # balanced ranges (split 0): partials for up to 2048 workgroups + batch
     n, s = msgl.paged_decode_workspace_size(64, 32, 8, 4096, 0)
-    assert s > 0 and s % 32 == 0
-    chunks = -(-4096 // s)
-    assert n >= chunks * 64 * 32 * (128 + 1) * 4
-    assert msgl.paged_decode_workspace_size(64, 32, 8, 200, 256)[0] == 0      # one chunk
+    assert s == 0
+    assert n >= (2048 + 64) * 32 * (128 + 1) * 4 + 64 * 2 * 4
+    assert msgl.paged_decode_workspace_size(5, 32, 8, 10, 0)[0] > 0
+    # fixed chunks: one partial per (chunk, request); none when one chunk suffices
+    n, s = msgl.paged_decode_workspace_size(64, 32, 8, 4096, 256)
+    assert s == 256 and n >= 16 * 64 * 32 * 129 * 4
+    assert msgl.paged_decode_workspace_size(64, 32, 8, 200, 256)[0] == 0
     assert msgl.paged_decode_workspace_size(0, 32, 8, 200, 256)[0] == 0
 
 

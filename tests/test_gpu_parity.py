@@ -226,6 +226,37 @@ def test_decode_empty_request():
     assert_close(out, ro, "empty request batch")
 
 
+@pytest.mark.parametrize("lens_kind", ["tiny", "zeros_at_edges", "many"])
+def test_decode_balanced_ranges_edge_cases(lens_kind):
+    """Balanced mode: fewer keys than workgroups, empty requests, >64 requests."""
+    banner(f"decode balanced {lens_kind}")
+    rng = np.random.default_rng(7)
+    if lens_kind == "tiny":
+        lens = rng.integers(1, 4, 300)                   # T ~ 600 keys
+    elif lens_kind == "zeros_at_edges":
+        lens = rng.integers(1, 900, 70)
+        lens[0] = lens[33] = lens[-1] = lens[-2] = 0
+    else:
+        lens = rng.integers(1, 2000, 200)
+    lens = lens.astype(np.int64)
+    gen_lens = np.maximum(lens, 1)                       # generator needs >= 1 key
+    inp = small_decode(67, 32, 8, gen_lens, num_slots=1 << 19)
+    u = Uploaded(inp)
+    u.store()
+    lens32 = lens.astype(np.int32)
+    out, lse = msgl.paged_decode(u.dq, u.k, u.v, u.pt, up(lens32), u.d_max, inp.sm_scale,
+                                 req_rows=u.d_rows)
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    sample = np.unique(np.concatenate([np.where(lens == 0)[0], np.arange(0, len(lens), 7),
+                                       [len(lens) - 1]]))
+    ro, rl = oracle.paged_decode(inp.dec_q[sample], kp, vp, inp.page_table,
+                                 inp.dec_req_rows[sample], lens32[sample], inp.sm_scale,
+                                 inp.num_kv_heads)
+    assert_close(out[torch.from_numpy(sample).cuda()], ro, f"balanced {lens_kind}")
+    assert_lse_close(lse[torch.from_numpy(sample).cuda()], rl, f"balanced {lens_kind}")
+
+
 def test_decode_zero_scale_is_mean_of_values():
     banner("decode sm_scale=0")
     inp = small_decode(66, 32, 8, [100, 37], num_slots=1024, sm_scale=0.0)
