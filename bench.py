@@ -275,6 +275,10 @@ def main(argv=None) -> int:
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--only", default="",
+                    help="run just this workload's steps (for profilers) and print its timing")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="also run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -292,6 +296,21 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {args.calibrate_copy} MiB three times")
+    if args.only:
+        inp_o = make_config(args.only)
+        run_o = Run(inp_o, args.split_tokens)
+        res_o = timed_steps(run_o, args.steps, args.warmup)
+        print(json.dumps({"only": args.only, **summarize(args.only, inp_o, run_o, res_o, args.steps)}))
+        return 0
 
     log("generating the headline decode batch")
     inp = make_config("C2")

@@ -21,15 +21,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
-  uint32_t u = __float_as_uint(x);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
+// Two fp32 -> packed bf16 (low half = lo), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // 16-byte global load/store through plain vector types (global_load_dwordx4).

@@ -127,13 +127,15 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
   const int row = p.req_rows ? p.req_rows[r] : r;
   const int32_t* pt = p.page_table + (int64_t)row * p.pt_stride;
 
-  // q rows of the group into LDS (ratio x 128 bf16, 16 bytes per lane step)
-  {
-    const uint16_t* qg = p.q + (int64_t)r * p.q_stride + (int64_t)g * R * kHeadDim;
-    __builtin_amdgcn_wave_barrier();
-    for (int u = lane; u < R * 16; u += 64)
-      *reinterpret_cast<u32x4*>(qs + 8 * u) = ld16(qg + 8 * u);
-    __builtin_amdgcn_wave_barrier();
+  // q rows of the group (ratio x 128 bf16) are loaded now and parked in LDS
+  // once the first page-table entries are in flight, so the two memory
+  // round trips of a segment start overlap.
+  const uint16_t* qg = p.q + (int64_t)r * p.q_stride + (int64_t)g * R * kHeadDim;
+  u32x4 qv[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int u = lane + 64 * k;
+    if (u < R * 16) qv[k] = ld16(qg + 8 * u);
   }
   // B operand of S^T = K Q^T: column c, k-slot (j, e) of step kk <-> head dim
   // 32*kk + 8*j + e.  Columns c >= ratio read a real row again; their output
@@ -156,6 +158,13 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
   // so each iteration waits on one memory latency (its K/V), not two.
   int na = pt[min(t0 + c, t1 - 1)];
   int nb = pt[min(t0 + 16 + c, t1 - 1)];
+  __builtin_amdgcn_wave_barrier();
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int u = lane + 64 * k;
+    if (u < R * 16) *reinterpret_cast<u32x4*>(qs + 8 * u) = qv[k];
+  }
+  __builtin_amdgcn_wave_barrier();
 
   for (int tb = t0; tb < t1; tb += kTile) {
     const char* ra = kbase + (int64_t)na * cs;

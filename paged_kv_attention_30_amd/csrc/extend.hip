@@ -65,10 +65,18 @@ __device__ __forceinline__ int vt_pos64(int k) {
   return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
 }
 
-__global__ void __launch_bounds__(256, 1)
+// Rescale threshold of the online softmax, in log2 units: the running
+// maximum is only moved (and O, l rescaled) when a new score exceeds it by
+// more than this, so p = 2^(s - m) stays <= 2^8 while most tiles skip the
+// rescale.  Softmax does not depend on the reference maximum, so this
+// changes rounding only.
+constexpr float kRescaleSlack = 8.f;
+
+__global__ void __launch_bounds__(256, 2)
 paged_extend_kernel(ExtendParams p) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kBN * kKPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kHeadDim * kVPitch];
+  // two K / V^T tile buffers: tile i+1 is written while tile i is read
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN * kKPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][kHeadDim * kVPitch];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -115,18 +123,31 @@ paged_extend_kernel(ExtendParams p) {
   const int ld_chunk = tid >> 6;
   const int64_t cs = p.cache_stride_bytes;
   const char* kb = p.k_cache + (int64_t)g * kHeadDim * 2;
-  const char* vb = p.v_cache + (int64_t)g * kHeadDim * 2;
+  const int64_t v_minus_k = p.v_cache - p.k_cache;
   const int vpos = vt_pos64(ld_key);
 
   u32x4 pk[4], pv[4];
   auto prefetch = [&](int tile) {
     const int key = min(tile * kBN + ld_key, kv_end - 1);
-    const int64_t slot = (int64_t)pt[key];
+    const char* src = kb + (int64_t)pt[key] * cs;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int off = (ld_chunk + 4 * u) * 16;
-      pk[u] = ld16(kb + slot * cs + off);
-      pv[u] = ld16(vb + slot * cs + off);
+      pk[u] = ld16(src + off);
+      pv[u] = ld16(src + v_minus_k + off);
+    }
+  };
+  auto stash = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int chunk = ld_chunk + 4 * u;
+      *reinterpret_cast<u32x4*>(&k_lds[buf][ld_key * kKPitch + chunk * 8]) = pk[u];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int d = chunk * 8 + 2 * e;
+        vt_lds[buf][d * kVPitch + vpos] = (uint16_t)(pv[u][e] & 0xffffu);
+        vt_lds[buf][(d + 1) * kVPitch + vpos] = (uint16_t)(pv[u][e] >> 16);
+      }
     }
   };
 
@@ -135,35 +156,33 @@ paged_extend_kernel(ExtendParams p) {
   for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY;   // reference maximum, log2 units
+  float l_run = 0.f;         // this lane's share of the running sum
+  const float c = p.scale_log2;
+
+  // the lowest visible-key bound among this wave's rows decides whether a
+  // tile needs the causal mask
+  int vis_min = vis_end;
+  vis_min = min(vis_min, __builtin_amdgcn_ds_bpermute(((lane ^ 32) << 2), vis_min));
+  for (int d = 16; d >= 1; d >>= 1)
+    vis_min = min(vis_min, __builtin_amdgcn_ds_bpermute(((lane ^ d) << 2), vis_min));
+  vis_min = __builtin_amdgcn_readfirstlane(vis_min);
 
   prefetch(0);
+  stash(0);
+  __syncthreads();
   for (int tile = 0; tile < n_tiles; ++tile) {
-    __syncthreads();
-    // registers -> LDS
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int chunk = ld_chunk + 4 * u;
-      *reinterpret_cast<u32x4*>(k_lds + ld_key * kKPitch + chunk * 8) = pk[u];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = chunk * 8 + 2 * e;
-        vt_lds[d * kVPitch + vpos] = (uint16_t)(pv[u][e] & 0xffffu);
-        vt_lds[(d + 1) * kVPitch + vpos] = (uint16_t)(pv[u][e] >> 16);
-      }
-    }
-    __syncthreads();
+    const int buf = tile & 1;
     if (tile + 1 < n_tiles) prefetch(tile + 1);
-
     const int kt = tile * kBN;
+
     // S^T for key blocks 0 and 1 of the tile
     f32x16 s[2];
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb2][i] = 0.f;
-      const uint16_t* krow = k_lds + (32 * kb2 + col) * kKPitch + 8 * jh;
+      const uint16_t* krow = &k_lds[buf][(32 * kb2 + col) * kKPitch + 8 * jh];
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * kk);
@@ -171,24 +190,41 @@ paged_extend_kernel(ExtendParams p) {
       }
     }
 
-    // scale, causal mask, running max
-    const bool need_mask = kt + kBN > vis_end;
-    float mt = -INFINITY;
+    // causal mask (only tiles that reach past some row's last visible key)
+    const bool masked_tile = kt + kBN > vis_min;
+    if (masked_tile) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = kt + 32 * kb2 + 8 * (i >> 2) + 4 * jh + (i & 3);
-        float v = s[kb2][i] * p.scale_log2;
-        if (need_mask && key >= vis_end) v = -INFINITY;
-        s[kb2][i] = v;
-        mt = fmaxf(mt, v);
-      }
+        for (int i = 0; i < 16; ++i) {
+          const int key = kt + 32 * kb2 + 8 * (i >> 2) + 4 * jh + (i & 3);
+          if (key >= vis_end) s[kb2][i] = c >= 0.f ? -INFINITY : INFINITY;
+        }
     }
-    mt = fmaxf(mt, shfl_xor(mt, 32));
-    const float m_new = fmaxf(m_run, mt);
-    const float alpha = fast_exp2(m_run - m_new);
-    m_run = m_new;
+    // tile maximum of c * s, in log2 units
+    float ext = s[0][0];
+    if (c >= 0.f) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ext = fmaxf(ext, s[kb2][i]);
+      ext = fmaxf(ext, shfl_xor(ext, 32));
+    } else {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) ext = fminf(ext, s[kb2][i]);
+      ext = fminf(ext, shfl_xor(ext, 32));
+    }
+    const float m_tile = c * ext;
+    if (__any(m_tile > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) acc[mb] = acc[mb] * alpha;
+    }
 
     u32x4 pb[4];
     float psum = 0.f;
@@ -197,24 +233,31 @@ paged_extend_kernel(ExtendParams p) {
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const int i0 = 8 * (u & 1) + 2 * e2;
-        const float p0 = fast_exp2(s[u >> 1][i0] - m_new);
-        const float p1 = fast_exp2(s[u >> 1][i0 + 1] - m_new);
+        float p0 = fast_exp2(fmaf(s[u >> 1][i0], c, -m_run));
+        float p1 = fast_exp2(fmaf(s[u >> 1][i0 + 1], c, -m_run));
+        if (masked_tile) {
+          const int key0 = kt + 32 * (u >> 1) + 8 * (i0 >> 2) + 4 * jh + (i0 & 3);
+          p0 = key0 < vis_end ? p0 : 0.f;
+          p1 = key0 + 1 < vis_end ? p1 : 0.f;
+        }
         pb[u][e2] = pack_bf16x2(p0, p1);
         psum += p0 + p1;
       }
     }
-    l_run = l_run * alpha + psum;
+    l_run += psum;
 
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      acc[mb] = acc[mb] * alpha;
-      const uint16_t* vrow = vt_lds + (32 * mb + col) * kVPitch + 8 * jh;
+      const uint16_t* vrow = &vt_lds[buf][(32 * mb + col) * kVPitch + 8 * jh];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(vrow + 16 * u);
         acc[mb] = mfma32x32x16(a, pb[u], acc[mb]);
       }
     }
+
+    if (tile + 1 < n_tiles) stash(buf ^ 1);
+    __syncthreads();
   }
 
   float l_tot = l_run + shfl_xor(l_run, 32);

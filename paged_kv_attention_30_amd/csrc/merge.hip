@@ -58,24 +58,40 @@ __global__ void __launch_bounds__(256) merge_kernel(MergeParams p) {
     step = 1;
   }
 
+  // One pass over the parts in order, eight at a time: their loads are
+  // issued together, then folded with a running maximum (o and the weight
+  // sum are rescaled whenever the maximum grows).  The fold order is the
+  // part order, so the result does not depend on scheduling.
   const int64_t rh = (int64_t)row * p.num_heads + h;
+  constexpr int kBatch = 8;
   float M = -INFINITY;
-  for (int s = 0; s < parts; ++s)
-    M = fmaxf(M, p.part_lse[(base + s * step) * p.num_heads + h]);
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  if (M != -INFINITY) {
-    for (int s = 0; s < parts; ++s) {
-      const int64_t ph = (base + s * step) * p.num_heads + h;
-      const float ls = p.part_lse[ph];
-      const float wgt = fast_exp2((ls - M) * kLog2e);
-      const f32x4 v = *reinterpret_cast<const f32x4*>(p.part_out + ph * p.head_dim + 4 * d4);
-      acc += v * wgt;
-      wsum += wgt;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int s0 = 0; s0 < parts; s0 += kBatch) {
+    const int n = min(kBatch, parts - s0);
+    float ls[kBatch];
+    f32x4 v[kBatch];
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (k < n) {
+        const int64_t ph = (base + (int64_t)(s0 + k) * step) * p.num_heads + h;
+        ls[k] = p.part_lse[ph];
+        v[k] = *reinterpret_cast<const f32x4*>(p.part_out + ph * p.head_dim + 4 * d4);
+      }
     }
-    acc = acc * (1.f / wsum);
+#pragma unroll
+    for (int k = 0; k < kBatch; ++k) {
+      if (k < n && ls[k] != -INFINITY) {
+        const float m_new = fmaxf(M, ls[k]);
+        const float scale_old = fast_exp2((M - m_new) * kLog2e);
+        const float w = fast_exp2((ls[k] - m_new) * kLog2e);
+        acc = acc * scale_old + v[k] * w;
+        wsum = wsum * scale_old + w;
+        M = m_new;
+      }
+    }
   }
+  if (M != -INFINITY) acc = acc * (1.f / wsum);
 
   if (p.out_bf16) {
     uint16_t* o = (uint16_t*)p.out + rh * p.head_dim + 4 * d4;
