@@ -68,6 +68,16 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i
+// receives element i % 4 of the 8-byte rows addressed by lanes 4k + i / 4
+// (k = 0..3), i.e. a 16x4 block of 16-bit values comes back transposed.
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(p));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -338,53 +338,65 @@ decode_balanced_kernel(DecodeParams p) {
   const int64_t T = uniform64(tl);
   // with fewer keys than workgroups, only the first T workgroups take keys
   const int64_t G = min((int64_t)Ggrid, T);
-  const int64_t start = (G > 0 && b < G) ? (int64_t)b * T / G : T;
-  const int64_t end = (G > 0 && b < G) ? (int64_t)(b + 1) * T / G : T;
+  // (64-bit division runs on the vector unit; move the results back to
+  // scalar registers)
+  const int64_t start = uniform64((G > 0 && b < G) ? (int64_t)b * T / G : T);
+  const int64_t end = uniform64((G > 0 && b < G) ? (int64_t)(b + 1) * T / G : T);
   const bool last = (b == Ggrid - 1);
   if (start == end && !last) return;
 
-  int64_t running = 0;
-  for (int base = 0; base < B; base += 64) {
-    if (running > end || (running == end && !last)) break;
-    const int i = base + lane;
-    const int Li = i < B ? max(p.seq_lens[i], 0) : 0;
-    const int incl = wave_incl_scan(Li);
-    const int64_t c0 = running + (incl - Li);
-    const int64_t c1 = running + incl;
-    bool own;
-    if (i >= B) own = false;
-    else if (Li > 0) own = c1 > start && c0 < end;
-    else own = (c0 >= start && c0 < end) || (last && c0 == T);
-    uint64_t mask = __ballot(own);
-    const int64_t next_running = running + __builtin_amdgcn_readlane(incl, 63);
-    while (mask) {
-      const int bit = __builtin_ctzll(mask);
-      mask &= mask - 1;
-      const int r = base + bit;
-      const int64_t r1 = running + __builtin_amdgcn_readlane(incl, bit);
-      const int64_t r0 = r1 - __builtin_amdgcn_readlane(Li, bit);
-      const bool writer = (w == 0 && blockIdx.y == 0 && lane == 0);
-      if (r1 == r0) {
-        write_empty(p, r, g, lane & 15, lane >> 4);
-        if (writer) {
-          p.meta[2 * r] = -1;
-          p.meta[2 * r + 1] = -1;
-        }
-        continue;
+  // Requests are visited in order; each step re-scans the lengths to find
+  // the next request (index > r_prev) whose keys meet this workgroup's range
+  // (or, for an empty request, whose position it owns), so nothing per-lane
+  // stays live across a segment.
+  const bool writer = (w == 0 && blockIdx.y == 0 && lane == 0);
+  int r_prev = -1;
+  while (true) {
+    int r = -1;
+    int64_t r0 = 0, r1 = 0;
+    int64_t running = 0;
+    for (int base = 0; base < B; base += 64) {
+      if (running > end || (running == end && !last)) break;
+      const int i = base + lane;
+      const int Li = i < B ? max(p.seq_lens[i], 0) : 0;
+      const int incl = wave_incl_scan(Li);
+      const int64_t c0 = running + (incl - Li);
+      const int64_t c1 = running + incl;
+      bool own;
+      if (i >= B || i <= r_prev) own = false;
+      else if (Li > 0) own = c1 > start && c0 < end;
+      else own = (c0 >= start && c0 < end) || (last && c0 == T);
+      const uint64_t mask = __ballot(own);
+      if (mask) {
+        const int bit = __builtin_ctzll(mask);
+        r = base + bit;
+        r1 = running + __builtin_amdgcn_readlane(incl, bit);
+        r0 = r1 - __builtin_amdgcn_readlane(Li, bit);
+        break;
       }
-      const int s0 = (int)(max(start, r0) - r0);
-      const int s1 = (int)(min(end, r1) - r0);
-      const bool whole = r0 >= start && r1 <= end;
-      attend_segment(p, vt, qs, r, g, s0, s1, whole, (int64_t)b + r);
-      if (writer) {
-        // workgroups holding the first and the last key of request r
-        const int64_t bf = ((r0 + 1) * G - 1) / T;
-        const int64_t bl = (r1 * G - 1) / T;
-        p.meta[2 * r] = whole ? -1 : (int32_t)bf;
-        p.meta[2 * r + 1] = whole ? -1 : (int32_t)bl;
-      }
+      running += __builtin_amdgcn_readlane(incl, 63);
     }
-    running = next_running;
+    if (r < 0) break;
+    r_prev = r;
+    if (r1 == r0) {
+      write_empty(p, r, g, lane & 15, lane >> 4);
+      if (writer) {
+        p.meta[2 * r] = -1;
+        p.meta[2 * r + 1] = -1;
+      }
+      continue;
+    }
+    const int s0 = (int)(max(start, r0) - r0);
+    const int s1 = (int)(min(end, r1) - r0);
+    const bool whole = r0 >= start && r1 <= end;
+    attend_segment(p, vt, qs, r, g, s0, s1, whole, (int64_t)b + r);
+    if (writer) {
+      // workgroups holding the first and the last key of request r
+      const int64_t bf = ((r0 + 1) * G - 1) / T;
+      const int64_t bl = (r1 * G - 1) / T;
+      p.meta[2 * r] = whole ? -1 : (int32_t)bf;
+      p.meta[2 * r + 1] = whole ? -1 : (int32_t)bl;
+    }
   }
 }
 
