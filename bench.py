@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "paged decode KV GB/s + extend TFLOP/s on 1 MI355X, % of roofline"
 KERNEL_SOURCES = ["decode.hip", "merge.hip", "common.hpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c2_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c2_traffic.md")
 
 WORKLOAD_TEXT = {
     "C2": "paged GQA decode + store_kv: Hq 32 / Hkv 8 / D 128, batch 64, kv lens U[512,4096], "
@@ -184,14 +184,26 @@ def cold_decode_ms(run: Run, reps: int = 10):
     return float(np.median(out))
 
 
-def load_traffic(khash: str, launches_bytes: float):
+def load_traffic(khash: str):
+    """Measured HBM bytes per decode call from the committed counter summary.
+
+    Returns None when there is no summary or it was taken on other kernel
+    sources (its recorded hash differs from the current one).
+    """
     if not os.path.exists(TRAFFIC_FILE):
         return None
+    vals = {}
     with open(TRAFFIC_FILE) as f:
-        d = json.load(f)
-    if d.get("kernel_hash") != khash:
+        for line in f:
+            if ":" in line and not line.startswith(("#", " ", "|")):
+                k, v = line.split(":", 1)
+                vals[k.strip()] = v.strip()
+    if vals.get("kernel_hash") != khash:
         return None
-    return d.get("traffic_bytes_per_launch")
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(inp, budget_s: float = 15.0):
@@ -325,12 +337,12 @@ def main(argv=None) -> int:
         head["decode_ms_cold_l2_mall_flushed"] = round(cold_decode_ms(run), 4)
 
     khash = kernel_hash()
-    traffic = load_traffic(khash, alg)
+    traffic = load_traffic(khash)
     roofline = {"bound": "hbm", "achieved": round(alg / (dec_ms * 1e-3) / 1e9, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": "paged_decode_kernel<8> + merge_kernel (one msgl_paged_decode call)",
+                "kernel": "decode_balanced_kernel<8> + merge_kernel (one msgl_paged_decode call)",
                 "alg_bytes_per_launch": alg, "avg_launch_ms": round(dec_ms, 4)}
     del run
     torch.cuda.empty_cache()
