@@ -126,10 +126,14 @@ paged_extend_kernel(ExtendParams p) {
   const int64_t v_minus_k = p.v_cache - p.k_cache;
   const int vpos = vt_pos64(ld_key);
 
+  // page-table entry of this lane's key, fetched one tile before its K/V so
+  // the table walk never sits in front of the data loads
+  auto slot_of = [&](int tile) -> int { return pt[min(tile * kBN + ld_key, kv_end - 1)]; };
+  int next_slot = slot_of(0);
   u32x4 pk[4], pv[4];
   auto prefetch = [&](int tile) {
-    const int key = min(tile * kBN + ld_key, kv_end - 1);
-    const char* src = kb + (int64_t)pt[key] * cs;
+    const char* src = kb + (int64_t)next_slot * cs;
+    next_slot = slot_of(tile + 1);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int off = (ld_chunk + 4 * u) * 16;
