@@ -12,15 +12,19 @@
 // gfx950 design: one workgroup of 4 waves takes one request, one kv head and
 // 128 query rows made of (q head of the group, query position) pairs, so the
 // K/V tiles staged in LDS serve the whole GQA group.  Per 64-key tile:
-// * every lane loads the page-table entry of one key and 16-byte pieces of
-//   that key's K and V rows into registers (prefetched one tile ahead),
-//   then writes K row-major and V transposed (V^T) into LDS;
-// * S^T = K Q^T on the 32x32x16 bf16 MFMA (A = K rows from LDS, B = q
-//   rows held in registers);
-// * online softmax per query row: every lane owns one query row, so the
-//   rescale is a per-lane scalar; the row max needs one cross-lane step;
-// * O^T = V^T P^T on MFMA, P^T being the S^T output repacked to bf16 in
-//   place (its C layout is the next MFMA's B layout).
+// * K and V go from HBM straight into LDS (global_load_lds_dwordx4: each
+//   wave instruction fills 1 KiB of LDS, lane l at +16 l), two stages deep,
+//   one barrier per tile; no register staging.  Which key / 16-byte piece a
+//   lane fetches is chosen so the LDS tiles come out XOR-swizzled for
+//   conflict-free operand reads.
+// * S^T = K Q^T on the 32x32x16 bf16 MFMA (A = K rows read from LDS, B = q
+//   rows held in registers).
+// * online softmax per query row (every lane owns one row); the reference
+//   maximum moves only when a score exceeds it by more than 2^8 (see
+//   kRescaleSlack), so most tiles skip the rescale of O.
+// * O^T = V^T P^T on MFMA: P^T is the S^T output repacked to bf16 in place
+//   (its C layout is the next MFMA's B layout); V^T operands come from the
+//   key-major V tile through the transposing LDS read (ds_read_b64_tr_b16).
 
 #include <float.h>
 
@@ -33,8 +37,14 @@ namespace {
 
 constexpr int kBN = 64;            // keys per tile
 constexpr int kRows = 128;         // (head, position) rows per workgroup
-constexpr int kKPitch = 136;       // LDS elements per key row of K (272 B)
-constexpr int kVPitch = 72;        // LDS elements per head-dim row of V^T (144 B)
+constexpr int kTileElems = kBN * kHeadDim;   // one K or V tile, bf16 elements
+
+// Rescale threshold of the online softmax, in log2 units: the running
+// maximum is only moved (and O, l rescaled) when a new score exceeds it by
+// more than this, so p = 2^(s - m) stays <= 2^8 while most tiles skip the
+// rescale.  Softmax does not depend on the reference maximum, so this
+// changes rounding only.
+constexpr float kRescaleSlack = 8.f;
 
 struct ExtendParams {
   uint16_t* out;
@@ -58,25 +68,29 @@ struct ExtendParams {
   float scale_log2;
 };
 
-// LDS position of key k (0..63) inside a V^T row: slot (l/32, e) of PV step u
-// holds key 16u + 8*(e/4) + 4*(l/32) + e%4, the keys the S^T output left in
-// lane l; stored at 16u + 8*(l/32) + e.  Swaps bits 2 and 3 of k.
-__device__ __forceinline__ int vt_pos64(int k) {
-  return (k & ~12) | ((k & 4) << 1) | ((k & 8) >> 1);
+// K tile: key-major rows of 16 sixteen-byte chunks; chunk c of key t sits at
+// position c ^ (t & 15), so 8 consecutive keys read at one chunk index hit 8
+// different bank groups.  Returns the element offset.
+__device__ __forceinline__ int k_off(int t, int chunk) {
+  return t * kHeadDim + 8 * (chunk ^ (t & 15));
 }
 
-// Rescale threshold of the online softmax, in log2 units: the running
-// maximum is only moved (and O, l rescaled) when a new score exceeds it by
-// more than this, so p = 2^(s - m) stays <= 2^8 while most tiles skip the
-// rescale.  Softmax does not depend on the reference maximum, so this
-// changes rounding only.
-constexpr float kRescaleSlack = 8.f;
+// V tile: key-major rows of 32 eight-byte groups; group cg of key t sits at
+// cg ^ (4 * (t & 3)), which keeps 16-byte pairs together and makes the
+// transposed reads of 4 keys x 16 dims conflict free.
+__device__ __forceinline__ int v_off(int t, int cg) {
+  return t * kHeadDim + 4 * (cg ^ (4 * (t & 3)));
+}
+
+__device__ __forceinline__ void load_to_lds(const char* src, uint16_t* lds_base) {
+  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+}
 
 __global__ void __launch_bounds__(256, 2)
 paged_extend_kernel(ExtendParams p) {
-  // two K / V^T tile buffers: tile i+1 is written while tile i is read
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kBN * kKPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][kHeadDim * kVPitch];
+  // [stage][K | V] tiles; stage t % 2 holds tile t
+  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][2][kTileElems];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -118,40 +132,31 @@ paged_extend_kernel(ExtendParams p) {
   const int kv_end = P + last_q + 1;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
 
-  // loader role: key tid % 64 of the tile, 16-byte chunks (tid / 64) + 4u
-  const int ld_key = tid & 63;
-  const int ld_chunk = tid >> 6;
+  // Loader role: wave w issues the 1-KiB LDS pieces 4w .. 4w+3 of each tile.
+  // Piece I holds keys 4I .. 4I+3; lane l of it lands on key 4I + l/16 at
+  // physical 16-byte position l % 16, i.e. K chunk (l%16) ^ (key & 15) and
+  // V 16-byte unit (l%16) ^ (2 * (key & 3)) of that key.
   const int64_t cs = p.cache_stride_bytes;
-  const char* kb = p.k_cache + (int64_t)g * kHeadDim * 2;
+  const char* kbase = p.k_cache + (int64_t)g * kHeadDim * 2;
   const int64_t v_minus_k = p.v_cache - p.k_cache;
-  const int vpos = vt_pos64(ld_key);
-
-  // page-table entry of this lane's key, fetched one tile before its K/V so
-  // the table walk never sits in front of the data loads
-  auto slot_of = [&](int tile) -> int { return pt[min(tile * kBN + ld_key, kv_end - 1)]; };
-  int next_slot = slot_of(0);
-  u32x4 pk[4], pv[4];
-  auto prefetch = [&](int tile) {
-    const char* src = kb + (int64_t)next_slot * cs;
-    next_slot = slot_of(tile + 1);
+  const int ld_keyoff = lane >> 4;     // key within a piece
+  const int ld_phys = lane & 15;       // physical 16-byte position within the row
+  int slots[4];
+  auto fetch_slots = [&](int tile) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int off = (ld_chunk + 4 * u) * 16;
-      pk[u] = ld16(src + off);
-      pv[u] = ld16(src + v_minus_k + off);
-    }
+    for (int u = 0; u < 4; ++u)
+      slots[u] = pt[min(tile * kBN + 4 * (4 * w + u) + ld_keyoff, kv_end - 1)];
   };
-  auto stash = [&](int buf) {
+  auto issue_tile = [&](int stage) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int chunk = ld_chunk + 4 * u;
-      *reinterpret_cast<u32x4*>(&k_lds[buf][ld_key * kKPitch + chunk * 8]) = pk[u];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = chunk * 8 + 2 * e;
-        vt_lds[buf][d * kVPitch + vpos] = (uint16_t)(pv[u][e] & 0xffffu);
-        vt_lds[buf][(d + 1) * kVPitch + vpos] = (uint16_t)(pv[u][e] >> 16);
-      }
+      const int piece = 4 * w + u;
+      const int key = 4 * piece + ld_keyoff;       // key within the tile
+      const char* rowp = kbase + (int64_t)slots[u] * cs;
+      const int kchunk = ld_phys ^ (key & 15);
+      const int vunit = ld_phys ^ (2 * (key & 3));
+      load_to_lds(rowp + 16 * kchunk, &tiles[stage][0][piece * 512]);
+      load_to_lds(rowp + v_minus_k + 16 * vunit, &tiles[stage][1][piece * 512]);
     }
   };
 
@@ -172,12 +177,27 @@ paged_extend_kernel(ExtendParams p) {
     vis_min = min(vis_min, __builtin_amdgcn_ds_bpermute(((lane ^ d) << 2), vis_min));
   vis_min = __builtin_amdgcn_readfirstlane(vis_min);
 
-  prefetch(0);
-  stash(0);
-  __syncthreads();
+  // transposed-read coordinates of this lane (16-lane group G = lane / 16):
+  // lane 4k + q of the group points at key k of the 4-key run, dims
+  // 32 mb + 16 (G & 1) + 4q
+  const int tr_key = (lane & 15) >> 2;
+  const int tr_cg = 4 * ((lane >> 4) & 1) + (lane & 3);
+
+  fetch_slots(0);
+  issue_tile(0);
+  if (n_tiles > 1) fetch_slots(1);
+
   for (int tile = 0; tile < n_tiles; ++tile) {
-    const int buf = tile & 1;
-    if (tile + 1 < n_tiles) prefetch(tile + 1);
+    const int st = tile & 1;
+    // this tile's pieces are in LDS once every wave's loads have landed
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tile + 1 < n_tiles) {
+      issue_tile(st ^ 1);                  // stage st^1 held tile-1: all waves are past it
+      if (tile + 2 < n_tiles) fetch_slots(tile + 2);
+    }
+    const uint16_t* kt_lds = tiles[st][0];
+    const uint16_t* vt_lds = tiles[st][1];
     const int kt = tile * kBN;
 
     // S^T for key blocks 0 and 1 of the tile
@@ -186,10 +206,10 @@ paged_extend_kernel(ExtendParams p) {
     for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb2][i] = 0.f;
-      const uint16_t* krow = &k_lds[buf][(32 * kb2 + col) * kKPitch + 8 * jh];
+      const int key = 32 * kb2 + col;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(krow + 16 * kk);
+        const u32x4 a = *reinterpret_cast<const u32x4*>(kt_lds + k_off(key, 2 * kk + jh));
         s[kb2] = mfma32x32x16(a, qb[kk], s[kb2]);
       }
     }
@@ -250,18 +270,18 @@ paged_extend_kernel(ExtendParams p) {
     }
     l_run += psum;
 
+    // O^T += V^T P^T: slot (jh, e) of step u is key 16u + 8(e/4) + 4jh + e%4
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb) {
-      const uint16_t* vrow = &vt_lds[buf][(32 * mb + col) * kVPitch + 8 * jh];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(vrow + 16 * u);
+        const int key_lo = 16 * u + 4 * jh + tr_key;
+        const u32x2 lo = lds_read_tr16(vt_lds + v_off(key_lo, 8 * mb + tr_cg));
+        const u32x2 hi = lds_read_tr16(vt_lds + v_off(key_lo + 8, 8 * mb + tr_cg));
+        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
         acc[mb] = mfma32x32x16(a, pb[u], acc[mb]);
       }
     }
-
-    if (tile + 1 < n_tiles) stash(buf ^ 1);
-    __syncthreads();
   }
 
   float l_tot = l_run + shfl_xor(l_run, 32);
