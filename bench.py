@@ -106,6 +106,8 @@ class Run:
             T = inp.ext_tokens
             self.ext_out = torch.empty((T, inp.num_q_heads, 128), dtype=torch.bfloat16, device="cuda")
             self.ext_lse = torch.empty((T, inp.num_q_heads), dtype=torch.float32, device="cuda")
+            self.ext_ws = msgl.alloc_workspace(msgl.paged_extend_workspace_size(
+                inp.num_extend, inp.num_q_heads, inp.num_kv_heads, t["e_max"], t["e_kv"]))
 
     def store(self):
         t = self.t
@@ -123,7 +125,7 @@ class Run:
         self.msgl.paged_extend(t["eq"], t["k"], t["v"], t["pt"], t["e_pre"], t["e_ext"],
                                t["e_off"], t["e_max"], t["e_kv"], inp.sm_scale,
                                req_rows=t["e_rows"], page_size=inp.page_size, out=self.ext_out,
-                               lse=self.ext_lse)
+                               lse=self.ext_lse, workspace=self.ext_ws)
 
     def step(self):
         self.store()

@@ -158,8 +158,14 @@ size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
  *   q          bf16 [T, num_q_heads, 128], row t at t * q_row_stride elements
  *   max_extend_len, max_kv_len   host upper bounds on E and P + E
  *   causal     must be 1 (the only mode the method uses)
- *   workspace  reserved; pass NULL / 0 (msgl_paged_extend_workspace_size
- *              returns the bytes required, currently 0)
+ *   workspace  optional, device memory of at least
+ *              msgl_paged_extend_workspace_size(...) bytes, 16-byte aligned,
+ *              owned by the caller and overwritten by the call.  With it, a
+ *              planning pass orders the (request, query tile) work items
+ *              longest first before the attention pass; with NULL the items
+ *              run last query tile first.  The results are bit-identical
+ *              either way; only the load balance differs.  A non-NULL
+ *              workspace smaller than required is MSGL_ERR_WORKSPACE.
  */
 int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_stride,
                       const void* k_cache, const void* v_cache, int64_t num_slots,
@@ -172,6 +178,9 @@ int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_st
                       int32_t causal, void* workspace, size_t workspace_bytes,
                       hipStream_t stream);
 
+/* Bytes of (optional) workspace msgl_paged_extend uses for its work list:
+ * 16 + 4 * batch * ceil(max_extend_len / (256 / (num_q_heads / num_kv_heads))),
+ * or 0 when there is nothing to plan. */
 size_t msgl_paged_extend_workspace_size(int32_t batch, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_extend_len, int32_t max_kv_len);

@@ -12,6 +12,7 @@ from .binding import (  # noqa: F401
     paged_decode,
     paged_decode_workspace_size,
     paged_extend,
+    paged_extend_workspace_size,
     merge_states,
     alloc_workspace,
 )

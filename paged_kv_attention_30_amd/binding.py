@@ -172,6 +172,15 @@ def paged_decode_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int,
     return int(n), int(s.value)
 
 
+def paged_extend_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int,
+                                max_extend_len: int, max_kv_len: int,
+                                head_dim: int = 128) -> int:
+    """Bytes of the (optional) work-list workspace of an extend call."""
+    lib = load()
+    return int(lib.msgl_paged_extend_workspace_size(batch, num_q_heads, num_kv_heads, head_dim,
+                                                    max_extend_len, max_kv_len))
+
+
 def alloc_workspace(nbytes: int, device=None) -> torch.Tensor | None:
     if nbytes <= 0:
         return None
@@ -237,8 +246,14 @@ def paged_extend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                  extend_lens: torch.Tensor, q_offsets: torch.Tensor, max_extend_len: int,
                  max_kv_len: int, sm_scale: float, req_rows: torch.Tensor | None = None,
                  page_size: int = 1, out: torch.Tensor | None = None,
-                 lse: torch.Tensor | None = None, want_lse: bool = True, stream=None):
-    """Causal extend.  q [T, Hq, 128] bf16; returns (out [T, Hq, 128], lse [T, Hq])."""
+                 lse: torch.Tensor | None = None, want_lse: bool = True,
+                 workspace: torch.Tensor | None = None, plan: bool = True, stream=None):
+    """Causal extend.  q [T, Hq, 128] bf16; returns (out [T, Hq, 128], lse [T, Hq]).
+
+    ``plan``: order the work longest first through a work-list workspace
+    (``workspace`` if given, else one allocated here); ``plan=False`` passes
+    no workspace.  The results are bit-identical either way.
+    """
     lib = load()
     _need(q, torch.bfloat16, "q", 3)
     n_slots, hkv, d, cstride = _pool_geometry(k_cache, v_cache)
@@ -267,11 +282,17 @@ def paged_extend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
         _need(lse, torch.float32, "lse", 2)
         if not lse.is_contiguous() or tuple(lse.shape) != (T, hq):
             raise ValueError("lse must be a contiguous [T, Hq] tensor")
+    if plan and workspace is None:
+        workspace = alloc_workspace(
+            paged_extend_workspace_size(B, hq, hkv, max_extend_len, max_kv_len, d), q.device)
+    if not plan:
+        workspace = None
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     st = lib.msgl_paged_extend(
         _ptr(out), _ptr(lse), _ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), n_slots, cstride,
         _ptr(page_table), page_table.stride(0), _ptr(req_rows), _ptr(prefix_lens),
         _ptr(extend_lens), _ptr(q_offsets), B, hq, hkv, d, page_size, max_extend_len, max_kv_len,
-        float(sm_scale), 1, None, 0, _stream(stream))
+        float(sm_scale), 1, _ptr(workspace), ws_bytes, _stream(stream))
     _check(st, "msgl_paged_extend")
     return out, lse
 

@@ -266,9 +266,9 @@ int msgl_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_st
 size_t msgl_paged_extend_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                         int32_t head_dim, int32_t max_extend_len,
                                         int32_t max_kv_len) {
-  (void)batch; (void)num_q_heads; (void)num_kv_heads; (void)head_dim;
-  (void)max_extend_len; (void)max_kv_len;
-  return 0;
+  (void)head_dim; (void)max_kv_len;
+  if (batch <= 0 || max_extend_len <= 0 || !ratio_ok(num_q_heads, num_kv_heads)) return 0;
+  return msgl::extend_workspace_bytes(batch, num_q_heads / num_kv_heads, max_extend_len);
 }
 
 int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_stride,
@@ -282,8 +282,6 @@ int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_st
                       int32_t causal, void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
   g_last_error[0] = 0;
-  (void)workspace;
-  (void)workspace_bytes;
   MSGL_CHECK(batch >= 0, MSGL_ERR_SHAPE, "batch %d is negative", batch);
   int st = validate_pool(k_cache, v_cache, num_slots, cache_row_stride, num_kv_heads, head_dim);
   if (st) return st;
@@ -307,6 +305,14 @@ int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_st
                  aligned(q_offsets, 4) && (!req_rows || aligned(req_rows, 4)) &&
                  (!lse_out || aligned(lse_out, 4)),
              MSGL_ERR_ALIGN, "int32/fp32 arrays must be 4-byte aligned");
+  const size_t ws_need = msgl::extend_workspace_bytes(batch, num_q_heads / num_kv_heads,
+                                                      max_extend_len);
+  MSGL_CHECK((int64_t)(ws_need - 16) / 4 * num_kv_heads < INT32_MAX, MSGL_ERR_SHAPE,
+             "batch x query tiles x num_kv_heads exceeds the launch grid");
+  MSGL_CHECK(!workspace || workspace_bytes >= ws_need, MSGL_ERR_WORKSPACE,
+             "extend workspace holds %zu bytes, the work list needs %zu", workspace_bytes, ws_need);
+  MSGL_CHECK(!workspace || aligned(workspace, 16), MSGL_ERR_ALIGN,
+             "workspace must be 16-byte aligned");
 
   msgl::ExtendArgs a;
   a.out = out;
@@ -315,6 +321,7 @@ int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_st
   a.q_stride = q_row_stride;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
+  a.num_slots = num_slots;
   a.cache_stride = cache_row_stride;
   a.page_table = page_table;
   a.pt_stride = page_table_stride;
@@ -329,6 +336,8 @@ int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_st
   a.max_extend_len = max_extend_len;
   a.max_kv_len = max_kv_len;
   a.sm_scale = sm_scale;
+  a.workspace = workspace;
+  a.workspace_bytes = workspace_bytes;
   a.stream = stream;
   return launch_status(msgl::launch_paged_extend(a), "paged_extend");
 }

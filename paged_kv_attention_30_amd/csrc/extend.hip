@@ -28,16 +28,35 @@
 
 #include <float.h>
 
+#include <type_traits>
+
 #include "common.hpp"
 #include "internal.hpp"
+
 
 namespace msgl {
 
 namespace {
 
 constexpr int kBN = 64;            // keys per tile
-constexpr int kRows = 128;         // (head, position) rows per workgroup
 constexpr int kTileElems = kBN * kHeadDim;   // one K or V tile, bf16 elements
+constexpr int kPieces = kTileElems * 2 / 1024;  // 1-KiB LDS pieces per K (or V) tile
+
+// s_waitcnt with only the vector-memory counter constrained (<= n).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 16, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(n) : "memory");
+}
+
+// Workgroup barrier without the memory fence __syncthreads() carries (that
+// fence waits for every outstanding load, including tiles meant to stay in
+// flight).  Callers order LDS themselves: every wave has waited for its own
+// tile loads (vmcnt) and consumed its LDS reads before arriving.
+__device__ __forceinline__ void tile_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's LDS accesses done
+  asm volatile("s_barrier" ::: "memory");
+}
 
 // Rescale threshold of the online softmax, in log2 units: the running
 // maximum is only moved (and O, l rescaled) when a new score exceeds it by
@@ -54,6 +73,7 @@ struct ExtendParams {
   const char* k_cache;
   const char* v_cache;
   int64_t cache_stride_bytes;
+  int64_t num_slots;
   const int32_t* page_table;
   int64_t pt_stride;
   const int32_t* req_rows;
@@ -61,11 +81,14 @@ struct ExtendParams {
   const int32_t* extend_lens;
   const int32_t* q_offsets;
   int32_t batch;
+  int32_t num_kv_heads;
   int32_t num_q_heads;
   int32_t ratio;
-  int32_t bq;              // query positions per workgroup = kRows / ratio
+  int32_t bq;              // query positions per workgroup = 32 * waves / ratio
   int32_t n_qtiles;
   float scale_log2;
+  const int32_t* work_count;   // sorted work list (null: natural order)
+  const int32_t* work_list;
 };
 
 // K tile: key-major rows of 16 sixteen-byte chunks; chunk c of key t sits at
@@ -82,22 +105,63 @@ __device__ __forceinline__ int v_off(int t, int cg) {
   return t * kHeadDim + 4 * (cg ^ (4 * (t & 3)));
 }
 
-__device__ __forceinline__ void load_to_lds(const char* src, uint16_t* lds_base) {
-  __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                   (__attribute__((address_space(3))) void*)lds_base, 16, 0, 0);
+// Direct global -> LDS loads, issued from inline assembly so the compiler
+// neither tracks them nor inserts waits for them: the loader below orders
+// them with explicit vmcnt waits (vector-memory loads complete in order).
+// Each wave instruction fills LDS at the wave-uniform base, lane l at
+// +size*l.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+__device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_addr(lds_base)) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* src, const void* lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_addr(lds_base)) : "memory", "m0");
 }
 
-__global__ void __launch_bounds__(256, 2)
+constexpr int kWaves = 8;          // two groups of four: one wave of each group per SIMD
+constexpr int kStages = 4;         // LDS K/V tile buffers
+constexpr int kPtRing = 4;         // page-table entry slots per wave
+constexpr int kPPW = kPieces / kWaves;   // 1-KiB pieces each wave loads per K (or V) tile
+
+// Eight waves of 32 query rows each.  Waves 0-3 ("lead") and 4-7 ("lag")
+// run the same tile loop half a tile apart: between two barriers the lead
+// waves compute S = K Q^T, softmax and O += P V of tile k while the lag
+// waves finish softmax and P V of tile k-1 and then compute S of tile k.
+// Each SIMD holds one wave of each group, so one wave's MFMA work runs
+// beside the other's softmax (exp and VALU) instead of both contending for
+// the same unit at the same time.
+__global__ void __launch_bounds__(kWaves * 64, 1)
 paged_extend_kernel(ExtendParams p) {
-  // [stage][K | V] tiles; stage t % 2 holds tile t
-  __shared__ __attribute__((aligned(16))) uint16_t tiles[2][2][kTileElems];
+  // stage t % kStages holds the K and V of tile t
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf[kStages * kTileElems];
+  __shared__ __attribute__((aligned(16))) uint16_t vbuf[kStages * kTileElems];
+  __shared__ __attribute__((aligned(16))) int32_t pt_ring[kWaves][kPtRing][kBN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
-  const int r = blockIdx.x % p.batch;
-  const int qt = p.n_qtiles - 1 - (int)(blockIdx.x / p.batch);   // heavy tiles first
-  const int g = blockIdx.y;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave index (uniform)
+  // Workgroup L takes kv head L % Hkv of work item L / Hkv.  Workgroups go
+  // to the XCDs round-robin, so with the head index varying fastest each
+  // XCD serves a fixed set of heads (their K/V stay in its L2) and receives
+  // the work items in list order: longest first when the planner sorted
+  // them, else last query tile first.
+  const int L = blockIdx.x;
+  const int g = L % p.num_kv_heads;
+  const int slot = L / p.num_kv_heads;
+  int r, qt;
+  if (p.work_list) {
+    if (slot >= *p.work_count) return;
+    const int item = p.work_list[slot];
+    r = item / p.n_qtiles;
+    qt = item - r * p.n_qtiles;
+  } else {
+    r = slot % p.batch;
+    qt = p.n_qtiles - 1 - slot / p.batch;
+  }
   const int E = p.extend_lens[r];
   const int q0 = qt * p.bq;
   if (q0 >= E) return;
@@ -125,6 +189,9 @@ paged_extend_kernel(ExtendParams p) {
     const uint16_t* qr = p.q + (int64_t)(qoff + qpos) * p.q_stride + (int64_t)head * kHeadDim;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qb[kk] = ld16(qr + 16 * kk + 8 * jh);
+    // q is in registers before the look-ahead loads start (a wait the
+    // compiler sees, so it adds none inside the tile loop)
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   // keys this workgroup needs: [0, kv_end)
@@ -132,31 +199,39 @@ paged_extend_kernel(ExtendParams p) {
   const int kv_end = P + last_q + 1;
   const int n_tiles = (kv_end + kBN - 1) / kBN;
 
-  // Loader role: wave w issues the 1-KiB LDS pieces 4w .. 4w+3 of each tile.
-  // Piece I holds keys 4I .. 4I+3; lane l of it lands on key 4I + l/16 at
-  // physical 16-byte position l % 16, i.e. K chunk (l%16) ^ (key & 15) and
-  // V 16-byte unit (l%16) ^ (2 * (key & 3)) of that key.
+  // Loader role: wave w issues the 1-KiB LDS pieces kPPW*w .. kPPW*w+kPPW-1
+  // of each tile.  Piece I holds keys 4I .. 4I+3; lane l of it lands on key
+  // 4I + l/16 at physical 16-byte position l % 16, i.e. K chunk
+  // (l%16) ^ (key & 15) and V 16-byte unit (l%16) ^ (2 * (key & 3)).
   const int64_t cs = p.cache_stride_bytes;
   const char* kbase = p.k_cache + (int64_t)g * kHeadDim * 2;
   const int64_t v_minus_k = p.v_cache - p.k_cache;
   const int ld_keyoff = lane >> 4;     // key within a piece
   const int ld_phys = lane & 15;       // physical 16-byte position within the row
-  int slots[4];
-  auto fetch_slots = [&](int tile) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      slots[u] = pt[min(tile * kBN + 4 * (4 * w + u) + ld_keyoff, kv_end - 1)];
+  // The page-table entries of tile t (64 ints) are fetched into this wave's
+  // ring slot t % kPtRing by one 4-byte direct load per lane; the K/V loads
+  // of tile t read their slots back from LDS.  Slots are clamped to the pool
+  // so that an address can never leave it.
+  int32_t* ring = &pt_ring[w][0][0];
+  auto fetch_pt = [&](int tile) {
+    dma4(pt + min(tile * kBN + lane, kv_end - 1), ring + (tile & (kPtRing - 1)) * kBN);
   };
-  auto issue_tile = [&](int stage) {
+  auto issue_tile = [&](int tile) {
+    const int stg = tile & (kStages - 1);
+    uint16_t* kd = kbuf + stg * kTileElems;
+    uint16_t* vd = vbuf + stg * kTileElems;
+    const int32_t* rs = ring + (tile & (kPtRing - 1)) * kBN;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int piece = 4 * w + u;
+    for (int u = 0; u < kPPW; ++u) {
+      const int piece = kPPW * w + u;
       const int key = 4 * piece + ld_keyoff;       // key within the tile
-      const char* rowp = kbase + (int64_t)slots[u] * cs;
+      int64_t slot = rs[key];
+      slot = slot < 0 ? 0 : (slot >= p.num_slots ? p.num_slots - 1 : slot);
+      const char* rowp = kbase + slot * cs;
       const int kchunk = ld_phys ^ (key & 15);
       const int vunit = ld_phys ^ (2 * (key & 3));
-      load_to_lds(rowp + 16 * kchunk, &tiles[stage][0][piece * 512]);
-      load_to_lds(rowp + v_minus_k + 16 * vunit, &tiles[stage][1][piece * 512]);
+      dma16(rowp + 16 * kchunk, kd + piece * 512);
+      dma16(rowp + v_minus_k + 16 * vunit, vd + piece * 512);
     }
   };
 
@@ -183,25 +258,10 @@ paged_extend_kernel(ExtendParams p) {
   const int tr_key = (lane & 15) >> 2;
   const int tr_cg = 4 * ((lane >> 4) & 1) + (lane & 3);
 
-  fetch_slots(0);
-  issue_tile(0);
-  if (n_tiles > 1) fetch_slots(1);
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int st = tile & 1;
-    // this tile's pieces are in LDS once every wave's loads have landed
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tile + 1 < n_tiles) {
-      issue_tile(st ^ 1);                  // stage st^1 held tile-1: all waves are past it
-      if (tile + 2 < n_tiles) fetch_slots(tile + 2);
-    }
-    const uint16_t* kt_lds = tiles[st][0];
-    const uint16_t* vt_lds = tiles[st][1];
-    const int kt = tile * kBN;
-
-    // S^T for key blocks 0 and 1 of the tile
-    f32x16 s[2];
+  // S^T for key blocks 0 and 1 of a tile
+  f32x16 s[2];
+  auto qk = [&](int tile) {
+    const uint16_t* kt_lds = kbuf + (tile & (kStages - 1)) * kTileElems;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
@@ -213,7 +273,12 @@ paged_extend_kernel(ExtendParams p) {
         s[kb2] = mfma32x32x16(a, qb[kk], s[kb2]);
       }
     }
+  };
 
+  // online softmax of the scores in s, then O^T += V^T P^T
+  auto softmax_pv = [&](int tile) {
+    const uint16_t* vt_lds = vbuf + (tile & (kStages - 1)) * kTileElems;
+    const int kt = tile * kBN;
     // causal mask (only tiles that reach past some row's last visible key)
     const bool masked_tile = kt + kBN > vis_min;
     if (masked_tile) {
@@ -282,7 +347,50 @@ paged_extend_kernel(ExtendParams p) {
         acc[mb] = mfma32x32x16(a, pb[u], acc[mb]);
       }
     }
+  };
+
+  // Load schedule per wave (vector-memory loads complete in order):
+  //   prologue: pt0 pt1 | tile0 pt2 | tile1 pt3
+  //   at barrier k: tile k+2 (into the stage of tile k-2), pt k+4
+  // Before barrier k a wave has its pieces of tile k and the table entries
+  // of tile k+2 (read right after the barrier); only tile k+1 and pt k+3
+  // may still be in flight.  The stage of tile k-2 is free at barrier k:
+  // its last reader, the lag group's P V of tile k-2, ran before barrier k.
+  // Tiles past the end re-read the last key, so every barrier sees the same
+  // loads in flight.
+  auto sync_tile = [&](int k) {
+    wait_vmcnt<2 * kPPW + 1>();
+    tile_barrier();
+    issue_tile(k + 2);
+    fetch_pt(k + 4);
+  };
+  fetch_pt(0);
+  fetch_pt(1);
+  wait_vmcnt<1>();                     // pt0 landed
+  issue_tile(0);
+  fetch_pt(2);
+  wait_vmcnt<2 * kPPW + 1>();          // pt1 landed
+  issue_tile(1);
+  fetch_pt(3);
+
+  // Both groups pass barriers 0 .. n_tiles.
+  if (w < kWaves / 2) {
+    for (int k = 0; k < n_tiles; ++k) {
+      sync_tile(k);
+      qk(k);
+      softmax_pv(k);
+    }
+    sync_tile(n_tiles);
+  } else {
+    sync_tile(0);
+    qk(0);
+    for (int k = 1; k <= n_tiles; ++k) {
+      sync_tile(k);
+      softmax_pv(k - 1);
+      if (k < n_tiles) qk(k);
+    }
   }
+  wait_vmcnt<0>();   // drain the look-ahead loads before the waves retire
 
   float l_tot = l_run + shfl_xor(l_run, 32);
   if (!row_valid) return;
@@ -302,7 +410,78 @@ paged_extend_kernel(ExtendParams p) {
   if (p.lse && jh == 0) p.lse[orow] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
+// ---------------------------------------------------------------------------
+// Work planner: one workgroup orders the (request, query tile) items by the
+// number of key tiles they visit, longest first (a counting sort over
+// kPlanBuckets buckets), so that the attention workgroups dispatched first
+// are the longest ones and the short ones fill in at the end.  The order of
+// items within a bucket is whatever the LDS atomics give; every item is
+// computed the same way wherever it lands, so results do not depend on it.
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanBuckets = kPlanThreads;
+
+struct PlanParams {
+  const int32_t* prefix_lens;
+  const int32_t* extend_lens;
+  int32_t batch;
+  int32_t n_qtiles;
+  int32_t bq;
+  int32_t shift;          // bucket = key tiles >> shift
+  int32_t* count;
+  int32_t* list;
+};
+
+__device__ __forceinline__ int plan_bucket(const PlanParams& p, int item) {
+  const int r = item / p.n_qtiles;
+  const int qt = item - r * p.n_qtiles;
+  const int E = p.extend_lens[r];
+  const int q0 = qt * p.bq;
+  if (q0 >= E) return -1;                    // no query rows: not an item
+  const int64_t kv_end = (int64_t)p.prefix_lens[r] + min(q0 + p.bq, E);
+  const int64_t tiles = (kv_end + kBN - 1) / kBN;
+  return (int)max((int64_t)0, min((int64_t)(kPlanBuckets - 1), tiles >> p.shift));
+}
+
+__global__ void __launch_bounds__(kPlanThreads) extend_plan_kernel(PlanParams p) {
+  __shared__ int hist[kPlanBuckets];
+  __shared__ int scan[kPlanBuckets];
+  const int tid = threadIdx.x;
+  const int total = p.batch * p.n_qtiles;
+  hist[tid] = 0;
+  __syncthreads();
+  for (int it = tid; it < total; it += kPlanThreads) {
+    const int b = plan_bucket(p, it);
+    if (b >= 0) atomicAdd(&hist[b], 1);
+  }
+  __syncthreads();
+  // inclusive scan over the buckets from the longest down
+  const int own = hist[kPlanBuckets - 1 - tid];
+  scan[tid] = own;
+  __syncthreads();
+  for (int d = 1; d < kPlanBuckets; d <<= 1) {
+    const int add = tid >= d ? scan[tid - d] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  hist[kPlanBuckets - 1 - tid] = scan[tid] - own;   // first list position of the bucket
+  if (tid == kPlanThreads - 1) p.count[0] = scan[tid];
+  __syncthreads();
+  for (int it = tid; it < total; it += kPlanThreads) {
+    const int b = plan_bucket(p, it);
+    if (b >= 0) p.list[atomicAdd(&hist[b], 1)] = it;
+  }
+}
+
+int extend_rows_per_block(int ratio) { return 32 * kWaves / ratio; }
+
 }  // namespace
+
+size_t extend_workspace_bytes(int64_t batch, int ratio, int64_t max_extend_len) {
+  const int64_t bq = extend_rows_per_block(ratio);
+  const int64_t nq = (max_extend_len + bq - 1) / bq;
+  return 16 + 4 * (size_t)(batch * nq);
+}
 
 hipError_t launch_paged_extend(const ExtendArgs& a) {
   ExtendParams p;
@@ -313,6 +492,7 @@ hipError_t launch_paged_extend(const ExtendArgs& a) {
   p.k_cache = (const char*)a.k_cache;
   p.v_cache = (const char*)a.v_cache;
   p.cache_stride_bytes = a.cache_stride * 2;
+  p.num_slots = a.num_slots;
   p.page_table = a.page_table;
   p.pt_stride = a.pt_stride;
   p.req_rows = a.req_rows;
@@ -322,12 +502,31 @@ hipError_t launch_paged_extend(const ExtendArgs& a) {
   p.batch = a.batch;
   p.num_q_heads = a.num_q_heads;
   p.ratio = a.num_q_heads / a.num_kv_heads;
-  p.bq = kRows / p.ratio;
-  p.n_qtiles = (a.max_extend_len + p.bq - 1) / p.bq;
   p.scale_log2 = a.sm_scale * kLog2e;
+  p.num_kv_heads = a.num_kv_heads;
+  p.bq = extend_rows_per_block(p.ratio);
+  p.n_qtiles = (a.max_extend_len + p.bq - 1) / p.bq;
+  p.work_count = nullptr;
+  p.work_list = nullptr;
   if (a.batch == 0 || p.n_qtiles == 0) return hipSuccess;
-  dim3 grid((unsigned)((int64_t)p.n_qtiles * a.batch), (unsigned)a.num_kv_heads);
-  hipLaunchKernelGGL(paged_extend_kernel, grid, dim3(256), 0, a.stream, p);
+  if (a.workspace) {
+    PlanParams pp;
+    pp.prefix_lens = a.prefix_lens;
+    pp.extend_lens = a.extend_lens;
+    pp.batch = a.batch;
+    pp.n_qtiles = p.n_qtiles;
+    pp.bq = p.bq;
+    int shift = 0;
+    while ((((int64_t)a.max_kv_len + kBN - 1) / kBN >> shift) >= kPlanBuckets) ++shift;
+    pp.shift = shift;
+    pp.count = (int32_t*)a.workspace;
+    pp.list = (int32_t*)((char*)a.workspace + 16);
+    hipLaunchKernelGGL(extend_plan_kernel, dim3(1), dim3(kPlanThreads), 0, a.stream, pp);
+    p.work_count = pp.count;
+    p.work_list = pp.list;
+  }
+  const int64_t blocks = (int64_t)p.n_qtiles * a.batch * a.num_kv_heads;
+  hipLaunchKernelGGL(paged_extend_kernel, dim3((unsigned)blocks), dim3(kWaves * 64), 0, a.stream, p);
   return hipGetLastError();
 }
 

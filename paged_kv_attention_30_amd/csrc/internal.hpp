@@ -62,6 +62,7 @@ struct ExtendArgs {
   int64_t q_stride;
   const void* k_cache;
   const void* v_cache;
+  int64_t num_slots;
   int64_t cache_stride;
   const int32_t* page_table;
   int64_t pt_stride;
@@ -76,8 +77,14 @@ struct ExtendArgs {
   int32_t max_extend_len;
   int32_t max_kv_len;
   float sm_scale;
+  void* workspace;         // optional work list (see extend_workspace_bytes) or null
+  size_t workspace_bytes;
   hipStream_t stream;
 };
+
+// Extend work list: 16 bytes of header (item count) plus one int32 per
+// (request, query tile) item.
+size_t extend_workspace_bytes(int64_t batch, int ratio, int64_t max_extend_len);
 
 struct MergeArgs {
   void* out;

@@ -107,14 +107,14 @@ def extend(lib, **kw):
     args = dict(out=FAKE, lse=FAKE, q=FAKE, q_stride=32 * 128, k=FAKE, v=FAKE2, slots=1024,
                 cstride=8 * 128, pt=FAKE, pt_stride=4096, rows=None, pre=FAKE, ext=FAKE, off=FAKE,
                 batch=2, hq=32, hkv=8, d=128, page=1, max_ext=512, max_kv=4096, scale=0.088,
-                causal=1)
+                causal=1, ws=None, ws_bytes=0)
     args.update(kw)
     return lib.msgl_paged_extend(args["out"], args["lse"], args["q"], args["q_stride"], args["k"],
                                  args["v"], args["slots"], args["cstride"], args["pt"],
                                  args["pt_stride"], args["rows"], args["pre"], args["ext"],
                                  args["off"], args["batch"], args["hq"], args["hkv"], args["d"],
                                  args["page"], args["max_ext"], args["max_kv"], args["scale"],
-                                 args["causal"], None, 0, None)
+                                 args["causal"], args["ws"], args["ws_bytes"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -131,6 +131,19 @@ def extend(lib, **kw):
 def test_extend_validation(lib, kw, code):
     st = extend(lib, **kw)
     assert st == code, (st, lib.msgl_last_error())
+
+
+def test_extend_workspace_rule(lib):
+    # 256 query rows per workgroup: ratio 4 -> 64 positions per query tile
+    assert msgl.paged_extend_workspace_size(8, 32, 8, 2048, 10240) == 16 + 4 * 8 * 32
+    assert msgl.paged_extend_workspace_size(3, 16, 16, 300, 300) == 16 + 4 * 3 * 2
+    assert msgl.paged_extend_workspace_size(1, 64, 4, 17, 17) == 16 + 4 * 1 * 2
+    assert msgl.paged_extend_workspace_size(0, 32, 8, 2048, 2048) == 0
+    assert msgl.paged_extend_workspace_size(4, 32, 8, 0, 2048) == 0
+    # batch 2, max_ext 512 -> 8 query tiles each
+    need = 16 + 4 * 2 * 8
+    assert extend(lib, ws=FAKE, ws_bytes=need - 4) == WS
+    assert extend(lib, ws=FAKE + 8, ws_bytes=need) == ALIGN
 
 
 def test_extend_zero_length_is_a_no_op(lib):

@@ -101,7 +101,11 @@ def test_full_extend_config_c3():
     check_store(u, inp, np.random.default_rng(3))
     kp, vp = stored_pool(inp)
     banner("C3: extend vs oracle sample")
-    check_extend(u, inp, kp, vp, "C3")
+    planned = check_extend(u, inp, kp, vp, "C3")
+    banner("C3: natural work order must be bit-identical to the planned one")
+    natural, _ = u.extend(plan=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(planned), bits(natural))
 
 
 def test_full_mixed_batch_c5_page16_and_page1():

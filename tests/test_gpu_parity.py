@@ -332,6 +332,24 @@ def test_extend_parity(case):
     assert_lse_close(lse, rl, f"extend case {case}")
 
 
+def test_extend_planned_order_is_bitwise_the_natural_order():
+    # the work-list planner only reorders workgroups; empty requests included
+    banner("extend planned vs natural order")
+    inp = small_extend(95, 32, 8, [(0, 0), (500, 300), (40, 0), (2000, 70), (0, 1), (129, 257)],
+                       num_slots=8192)
+    u = Uploaded(inp)
+    u.store()
+    op, lp = u.extend(plan=True)
+    on, ln = u.extend(plan=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(op), bits(on))
+    assert np.array_equal(lp.cpu().numpy().view(np.uint32), ln.cpu().numpy().view(np.uint32))
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle_extend(inp, kp, vp)
+    assert_close(op, ro, "extend planned")
+    assert_lse_close(lp, rl, "extend planned lse")
+
+
 def test_extend_with_shared_prefix_and_page_size_16():
     banner("extend shared prefix, page 16 vs 1")
     inp = small_extend(90, 32, 8, [(64, 100), (64, 37), (128, 64)], page_size=16,
