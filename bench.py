@@ -109,23 +109,27 @@ class Run:
             self.ext_ws = msgl.alloc_workspace(msgl.paged_extend_workspace_size(
                 inp.num_extend, inp.num_q_heads, inp.num_kv_heads, t["e_max"], t["e_kv"]))
 
+        # validated and marshalled once; each phase is then one library call
+        self.p_store = msgl.plan_store_kv(t["k"], t["v"], t["k_new"], t["v_new"], t["out_loc"])
+        if inp.num_decode:
+            self.p_dec = msgl.plan_paged_decode(
+                t["dq"], t["k"], t["v"], t["pt"], t["d_lens"], t["d_max"], inp.sm_scale,
+                req_rows=t["d_rows"], page_size=inp.page_size, split_tokens=split_tokens,
+                out=self.dec_out, lse=self.dec_lse, workspace=self.ws)
+        if inp.num_extend:
+            self.p_ext = msgl.plan_paged_extend(
+                t["eq"], t["k"], t["v"], t["pt"], t["e_pre"], t["e_ext"], t["e_off"], t["e_max"],
+                t["e_kv"], inp.sm_scale, req_rows=t["e_rows"], page_size=inp.page_size,
+                out=self.ext_out, lse=self.ext_lse, workspace=self.ext_ws)
+
     def store(self):
-        t = self.t
-        self.msgl.store_kv(t["k"], t["v"], t["k_new"], t["v_new"], t["out_loc"])
+        self.p_store.run()
 
     def decode(self):
-        t, inp = self.t, self.inp
-        self.msgl.paged_decode(t["dq"], t["k"], t["v"], t["pt"], t["d_lens"], t["d_max"],
-                               inp.sm_scale, req_rows=t["d_rows"], page_size=inp.page_size,
-                               split_tokens=self.split, out=self.dec_out, lse=self.dec_lse,
-                               workspace=self.ws)
+        self.p_dec.run()
 
     def extend(self):
-        t, inp = self.t, self.inp
-        self.msgl.paged_extend(t["eq"], t["k"], t["v"], t["pt"], t["e_pre"], t["e_ext"],
-                               t["e_off"], t["e_max"], t["e_kv"], inp.sm_scale,
-                               req_rows=t["e_rows"], page_size=inp.page_size, out=self.ext_out,
-                               lse=self.ext_lse, workspace=self.ext_ws)
+        self.p_ext.run()
 
     def step(self):
         self.store()
@@ -134,51 +138,100 @@ class Run:
         if self.inp.num_extend:
             self.extend()
 
+    def phases(self):
+        ph = [("store", self.store)]
+        if self.inp.num_decode:
+            ph.append(("decode", self.decode))
+        if self.inp.num_extend:
+            ph.append(("extend", self.extend))
+        return ph
 
-def timed_steps(run: Run, steps: int, warmup: int):
-    """Warm up, then time exactly ``steps`` steps; per-phase HIP events inside."""
+    def capture(self):
+        """Record each phase of a step as a HIP graph (as a serving loop replays its
+        decode step), so the timed loop launches graphs and host-side argument
+        marshalling never leaves the GPU idle between kernels."""
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(2):
+                self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graphs = {}
+        for name, fn in self.phases():
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                fn()
+            self.graphs[name] = g
+        torch.cuda.synchronize()
+
+
+def timed_steps(run: Run, steps: int, warmup: int, graphs: bool = False):
+    """Warm up, then time exactly ``steps`` whole steps, then each phase alone.
+
+    The steps are bracketed by two HIP events only (an event recorded between
+    two kernels leaves the GPU idle for several microseconds, so none sits
+    inside the timed steps).  Each phase's average duration then comes from
+    ``steps`` back-to-back calls of that phase alone, bracketed the same way.
+    Each phase is one planned library call (validated and marshalled when the
+    run was set up), or with ``graphs`` the replay of its captured graph."""
     torch = run.torch
+    if graphs:
+        run.capture()
+        calls = {name: g.replay for name, g in run.graphs.items()}
+    else:
+        calls = dict(run.phases())
+    order = [c for c in ("store", "decode", "extend") if c in calls]
+
+    def step():
+        for c in order:
+            calls[c]()
+
     for _ in range(warmup):
-        run.step()
+        step()
     torch.cuda.synchronize()
-    evs = []
-    t0 = time.perf_counter()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
     start.record()
     for _ in range(steps):
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-        e[0].record()
-        run.store()
-        e[1].record()
-        if run.inp.num_decode:
-            run.decode()
-        e[2].record()
-        if run.inp.num_extend:
-            run.extend()
-        e[3].record()
-        evs.append(e)
+        step()
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(end)
-    store_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in evs]
-    ext_ms = [e[2].elapsed_time(e[3]) for e in evs]
-    return dict(total_ms=total_ms, wall_s=wall, store_ms=store_ms, dec_ms=dec_ms, ext_ms=ext_ms)
-
-
-def cold_decode_ms(run: Run, reps: int = 10):
-    """Decode time with L2 and the 256 MB Infinity Cache flushed before each call."""
-    torch = run.torch
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-    out = []
-    for _ in range(reps):
-        scratch.add_(1)
+    phase = {}
+    for c in order:
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
-        run.decode()
+        for _ in range(steps):
+            calls[c]()
+        b.record()
+        torch.cuda.synchronize()
+        phase[c] = a.elapsed_time(b) / steps
+    return dict(total_ms=total_ms, wall_s=wall, store_ms=[phase["store"]],
+                dec_ms=[phase.get("decode", 0.0)], ext_ms=[phase.get("extend", 0.0)])
+
+
+def cold_decode_ms(run: Run, reps: int = 10):
+    """Decode time with L2 and the 256 MB Infinity Cache flushed before each call.
+
+    The flush reads a 1 GiB buffer (a read leaves the caches holding clean
+    lines of it, so the decode pays no write-backs for the flush)."""
+    torch = run.torch
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink = torch.empty((), dtype=torch.float32, device="cuda")
+    out = []
+    graphs = getattr(run, "graphs", None)
+    call = graphs["decode"].replay if graphs else run.decode
+    for _ in range(reps):
+        torch.sum(scratch, out=sink)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
         b.record()
         torch.cuda.synchronize()
         out.append(a.elapsed_time(b))
@@ -208,8 +261,10 @@ def load_traffic(khash: str):
         return None
 
 
-def cpu_baseline(inp, budget_s: float = 15.0):
-    """Time the oracle on a bounded sample of the decode workload (rank 0)."""
+def cpu_baseline(inp, budget_s: float = 12.0):
+    """Time the oracle on a bounded sample of the decode workload (rank 0):
+    passes over the batch's requests, one request at a time, until about
+    ``budget_s`` seconds of CPU work are done."""
     import oracle
     from workloads import metrics
     try:
@@ -222,8 +277,9 @@ def cpu_baseline(inp, budget_s: float = 15.0):
         done = 0
         t0 = time.perf_counter()
         kv_bytes = 0
-        while done < inp.num_decode and time.perf_counter() - t0 < budget_s:
-            sel = slice(done, done + 1)
+        while time.perf_counter() - t0 < budget_s:
+            i = done % inp.num_decode
+            sel = slice(i, i + 1)
             oracle.paged_decode(inp.dec_q[sel], kp, vp, inp.page_table, inp.dec_req_rows[sel],
                                 inp.dec_seq_lens[sel], inp.sm_scale, inp.num_kv_heads)
             kv_bytes += metrics.decode_kv_bytes(inp.page_table, inp.dec_req_rows[sel],
@@ -234,8 +290,9 @@ def cpu_baseline(inp, budget_s: float = 15.0):
         if ctx is not None:
             ctx.__exit__(None, None, None)
     return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 numpy oracle decode of the first {done} of {inp.num_decode} requests "
-                      f"of the headline batch ({kv_bytes / 1e6:.1f} MB distinct K/V) in {dt:.1f} s, "
+            "sample": f"fp64 numpy oracle decode, one request at a time, {done} request-decodes "
+                      f"({done / inp.num_decode:.1f} passes over the {inp.num_decode}-request headline "
+                      f"batch, {kv_bytes / 1e6:.1f} MB of K/V) in {dt:.1f} s, "
                       f"BLAS limited to 1 thread; host {platform.processor() or platform.machine()}, "
                       f"{os.cpu_count()} logical CPUs visible"}
 
@@ -289,6 +346,8 @@ def main(argv=None) -> int:
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--graphs", action="store_true",
+                    help="replay each phase from a captured HIP graph instead of planned calls")
     ap.add_argument("--only", default="",
                     help="run just this workload's steps (for profilers) and print its timing")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -322,7 +381,7 @@ def main(argv=None) -> int:
     if args.only:
         inp_o = make_config(args.only)
         run_o = Run(inp_o, args.split_tokens)
-        res_o = timed_steps(run_o, args.steps, args.warmup)
+        res_o = timed_steps(run_o, args.steps, args.warmup, args.graphs)
         print(json.dumps({"only": args.only, **summarize(args.only, inp_o, run_o, res_o, args.steps)}))
         return 0
 
@@ -330,7 +389,7 @@ def main(argv=None) -> int:
     inp = make_config("C2")
     run = Run(inp, args.split_tokens)
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
-    res = timed_steps(run, args.steps, args.warmup)
+    res = timed_steps(run, args.steps, args.warmup, args.graphs)
     head = summarize("C2", inp, run, res, args.steps)
     kv, alg, dec_ms = decode_figures(inp, res, args.steps)
     step_s = res["total_ms"] * 1e-3 / args.steps
@@ -354,7 +413,7 @@ def main(argv=None) -> int:
         log(f"workload {name}")
         inp_x = make_config(name)
         run_x = Run(inp_x, args.split_tokens)
-        res_x = timed_steps(run_x, max(5, args.steps // 5), 3)
+        res_x = timed_steps(run_x, max(5, args.steps // 5), 3, args.graphs)
         extras[name] = summarize(name, inp_x, run_x, res_x, max(5, args.steps // 5))
         del run_x
         torch.cuda.empty_cache()
@@ -378,7 +437,8 @@ def main(argv=None) -> int:
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": WORKLOAD_TEXT["C2"], "step": "store_kv(64 rows) + paged_decode (+LSE merge)",
-                   "split_tokens": head.get("decode_split_tokens"), "page_size": 1},
+                   "split_tokens": head.get("decode_split_tokens"), "page_size": 1,
+                   "launch": "hip_graph_replay" if args.graphs else "planned_calls"},
         "roofline": roofline,
         "cpu_baseline": cpu,
         "extras": extras,

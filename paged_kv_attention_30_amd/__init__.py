@@ -6,6 +6,10 @@ declared in ``include/msgl.h``); this package is the thin ctypes binding.
 
 from .binding import (  # noqa: F401
     MsglError,
+    PlannedCall,
+    plan_store_kv,
+    plan_paged_decode,
+    plan_paged_extend,
     load,
     version,
     store_kv,

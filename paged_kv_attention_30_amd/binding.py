@@ -120,6 +120,29 @@ def version() -> int:
     return load().msgl_version()
 
 
+class PlannedCall:
+    """One validated, marshalled library call.
+
+    ``plan_*`` functions check shapes and dtypes, allocate what the caller
+    left out and fix every argument except the stream; ``run()`` then issues
+    the C call alone (one ctypes call), e.g. once per layer of a model whose
+    batch metadata is fixed for the step.  The tensors the plan refers to must
+    stay alive and keep their storage; ``run()`` returns ``outputs``.
+    """
+
+    __slots__ = ("_fn", "_args", "_name", "outputs", "_keep")
+
+    def __init__(self, fn, args, name, outputs, keep):
+        self._fn, self._args, self._name = fn, tuple(args), name
+        self.outputs, self._keep = outputs, keep
+
+    def run(self, stream=None):
+        st = self._fn(*self._args, _stream(stream))
+        if st:
+            _check(st, self._name)
+        return self.outputs
+
+
 # ---------------------------------------------------------------------------
 # store_kv
 # ---------------------------------------------------------------------------
@@ -127,6 +150,12 @@ def version() -> int:
 def store_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
              v_new: torch.Tensor, out_loc: torch.Tensor, stream=None) -> None:
     """k_cache[out_loc[i]] = k_new[i] and likewise for V (in place)."""
+    plan_store_kv(k_cache, v_cache, k_new, v_new, out_loc).run(stream)
+
+
+def plan_store_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
+                  v_new: torch.Tensor, out_loc: torch.Tensor) -> PlannedCall:
+    """Planned form of :func:`store_kv`."""
     lib = load()
     if k_cache.dim() != 3 or k_new.dim() != 3:
         raise ValueError("k_cache [slots, Hkv, D] and k_new [n, Hkv, D] expected")
@@ -149,12 +178,11 @@ def store_kv(k_cache: torch.Tensor, v_cache: torch.Tensor, k_new: torch.Tensor,
         raise ValueError("K and V planes must share row strides")
     if out_loc.dim() != 1 or out_loc.shape[0] != k_new.shape[0] or not out_loc.is_contiguous():
         raise ValueError("out_loc must be a contiguous [n] vector")
-    st = lib.msgl_store_kv(
-        _ptr(k_cache), _ptr(v_cache), n_slots, k_cache.stride(0), _ptr(k_new), _ptr(v_new),
-        k_new.stride(0), _ptr(out_loc), INDEX_I64 if out_loc.dtype == torch.int64 else INDEX_I32,
-        k_new.shape[0], hkv, d, DTYPE_BF16 if k_cache.dtype == torch.bfloat16 else DTYPE_F32,
-        _stream(stream))
-    _check(st, "msgl_store_kv")
+    args = (_ptr(k_cache), _ptr(v_cache), n_slots, k_cache.stride(0), _ptr(k_new), _ptr(v_new),
+            k_new.stride(0), _ptr(out_loc), INDEX_I64 if out_loc.dtype == torch.int64 else INDEX_I32,
+            k_new.shape[0], hkv, d, DTYPE_BF16 if k_cache.dtype == torch.bfloat16 else DTYPE_F32)
+    return PlannedCall(lib.msgl_store_kv, args, "msgl_store_kv", None,
+                       (k_cache, v_cache, k_new, v_new, out_loc))
 
 
 # ---------------------------------------------------------------------------
@@ -197,6 +225,19 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
 
     Returns ``(out [B, Hq, 128] bf16, lse [B, Hq] fp32 or None)``.
     """
+    return plan_paged_decode(q, k_cache, v_cache, page_table, seq_lens, max_seq_len, sm_scale,
+                             req_rows, page_size, split_tokens, out, lse, want_lse,
+                             workspace).run(stream)
+
+
+def plan_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                      sm_scale: float, req_rows: torch.Tensor | None = None,
+                      page_size: int = 1, split_tokens: int = 0,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                      want_lse: bool = True,
+                      workspace: torch.Tensor | None = None) -> PlannedCall:
+    """Planned form of :func:`paged_decode`; ``run()`` returns ``(out, lse)``."""
     lib = load()
     _need(q, torch.bfloat16, "q", 3)
     n_slots, hkv, d, cstride = _pool_geometry(k_cache, v_cache)
@@ -228,13 +269,12 @@ def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if workspace is None and need:
         workspace = alloc_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.msgl_paged_decode(
-        _ptr(out), _ptr(lse), _ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), n_slots, cstride,
-        _ptr(page_table), page_table.stride(0), _ptr(req_rows), _ptr(seq_lens), B, hq, hkv, d,
-        page_size, max_seq_len, float(sm_scale), split_tokens, _ptr(workspace), ws_bytes,
-        _stream(stream))
-    _check(st, "msgl_paged_decode")
-    return out, lse
+    args = (_ptr(out), _ptr(lse), _ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), n_slots,
+            cstride, _ptr(page_table), page_table.stride(0), _ptr(req_rows), _ptr(seq_lens), B, hq,
+            hkv, d, page_size, max_seq_len, float(sm_scale), split_tokens, _ptr(workspace),
+            ws_bytes)
+    return PlannedCall(lib.msgl_paged_decode, args, "msgl_paged_decode", (out, lse),
+                       (q, k_cache, v_cache, page_table, seq_lens, req_rows, workspace))
 
 
 # ---------------------------------------------------------------------------
@@ -254,6 +294,19 @@ def paged_extend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     (``workspace`` if given, else one allocated here); ``plan=False`` passes
     no workspace.  The results are bit-identical either way.
     """
+    return plan_paged_extend(q, k_cache, v_cache, page_table, prefix_lens, extend_lens,
+                             q_offsets, max_extend_len, max_kv_len, sm_scale, req_rows,
+                             page_size, out, lse, want_lse, workspace, plan).run(stream)
+
+
+def plan_paged_extend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      page_table: torch.Tensor, prefix_lens: torch.Tensor,
+                      extend_lens: torch.Tensor, q_offsets: torch.Tensor, max_extend_len: int,
+                      max_kv_len: int, sm_scale: float, req_rows: torch.Tensor | None = None,
+                      page_size: int = 1, out: torch.Tensor | None = None,
+                      lse: torch.Tensor | None = None, want_lse: bool = True,
+                      workspace: torch.Tensor | None = None, plan: bool = True) -> PlannedCall:
+    """Planned form of :func:`paged_extend`; ``run()`` returns ``(out, lse)``."""
     lib = load()
     _need(q, torch.bfloat16, "q", 3)
     n_slots, hkv, d, cstride = _pool_geometry(k_cache, v_cache)
@@ -288,13 +341,13 @@ def paged_extend(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
     if not plan:
         workspace = None
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    st = lib.msgl_paged_extend(
-        _ptr(out), _ptr(lse), _ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), n_slots, cstride,
-        _ptr(page_table), page_table.stride(0), _ptr(req_rows), _ptr(prefix_lens),
-        _ptr(extend_lens), _ptr(q_offsets), B, hq, hkv, d, page_size, max_extend_len, max_kv_len,
-        float(sm_scale), 1, _ptr(workspace), ws_bytes, _stream(stream))
-    _check(st, "msgl_paged_extend")
-    return out, lse
+    args = (_ptr(out), _ptr(lse), _ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), n_slots,
+            cstride, _ptr(page_table), page_table.stride(0), _ptr(req_rows), _ptr(prefix_lens),
+            _ptr(extend_lens), _ptr(q_offsets), B, hq, hkv, d, page_size, max_extend_len,
+            max_kv_len, float(sm_scale), 1, _ptr(workspace), ws_bytes)
+    return PlannedCall(lib.msgl_paged_extend, args, "msgl_paged_extend", (out, lse),
+                       (q, k_cache, v_cache, page_table, prefix_lens, extend_lens, q_offsets,
+                        req_rows, workspace))
 
 
 # ---------------------------------------------------------------------------

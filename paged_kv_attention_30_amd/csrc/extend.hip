@@ -99,10 +99,12 @@ __device__ __forceinline__ int k_off(int t, int chunk) {
 }
 
 // V tile: key-major rows of 32 eight-byte groups; group cg of key t sits at
-// cg ^ (4 * (t & 3)), which keeps 16-byte pairs together and makes the
-// transposed reads of 4 keys x 16 dims conflict free.
+// cg ^ (8 * (t & 3)).  A transposed read serves 32 lanes = 4 keys (t & 3
+// distinct) x 8 consecutive groups at once; the XOR sends the four keys to
+// four disjoint blocks of 8 bank slots, so the read is conflict free, and it
+// keeps the 16-byte pairs a direct load writes together.
 __device__ __forceinline__ int v_off(int t, int cg) {
-  return t * kHeadDim + 4 * (cg ^ (4 * (t & 3)));
+  return t * kHeadDim + 4 * (cg ^ (8 * (t & 3)));
 }
 
 // Direct global -> LDS loads, issued from inline assembly so the compiler
@@ -202,7 +204,7 @@ paged_extend_kernel(ExtendParams p) {
   // Loader role: wave w issues the 1-KiB LDS pieces kPPW*w .. kPPW*w+kPPW-1
   // of each tile.  Piece I holds keys 4I .. 4I+3; lane l of it lands on key
   // 4I + l/16 at physical 16-byte position l % 16, i.e. K chunk
-  // (l%16) ^ (key & 15) and V 16-byte unit (l%16) ^ (2 * (key & 3)).
+  // (l%16) ^ (key & 15) and V 16-byte unit (l%16) ^ (4 * (key & 3)).
   const int64_t cs = p.cache_stride_bytes;
   const char* kbase = p.k_cache + (int64_t)g * kHeadDim * 2;
   const int64_t v_minus_k = p.v_cache - p.k_cache;
@@ -221,15 +223,19 @@ paged_extend_kernel(ExtendParams p) {
     uint16_t* kd = kbuf + stg * kTileElems;
     uint16_t* vd = vbuf + stg * kTileElems;
     const int32_t* rs = ring + (tile & (kPtRing - 1)) * kBN;
+    // all table reads first: the loads below are opaque to the compiler,
+    // so a read placed after one of them would wait for it
+    int64_t slot[kPPW];
+#pragma unroll
+    for (int u = 0; u < kPPW; ++u) slot[u] = rs[4 * (kPPW * w + u) + ld_keyoff];
 #pragma unroll
     for (int u = 0; u < kPPW; ++u) {
       const int piece = kPPW * w + u;
       const int key = 4 * piece + ld_keyoff;       // key within the tile
-      int64_t slot = rs[key];
-      slot = slot < 0 ? 0 : (slot >= p.num_slots ? p.num_slots - 1 : slot);
-      const char* rowp = kbase + slot * cs;
+      const int64_t sl = slot[u] < 0 ? 0 : (slot[u] >= p.num_slots ? p.num_slots - 1 : slot[u]);
+      const char* rowp = kbase + sl * cs;
       const int kchunk = ld_phys ^ (key & 15);
-      const int vunit = ld_phys ^ (2 * (key & 3));
+      const int vunit = ld_phys ^ (4 * (key & 3));
       dma16(rowp + 16 * kchunk, kd + piece * 512);
       dma16(rowp + v_minus_k + 16 * vunit, vd + piece * 512);
     }
