@@ -296,6 +296,8 @@ int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_st
              "q_row_stride %lld < num_q_heads*head_dim", (long long)q_row_stride);
   MSGL_CHECK(page_table_stride >= max_kv_len, MSGL_ERR_SHAPE,
              "page_table_stride %lld < max_kv_len %d", (long long)page_table_stride, max_kv_len);
+  MSGL_CHECK(cache_row_stride * 2 <= (int64_t)UINT32_MAX, MSGL_ERR_SHAPE,
+             "cache_row_stride %lld: a pool row must be under 4 GiB", (long long)cache_row_stride);
   if (batch == 0 || max_extend_len == 0) return MSGL_OK;
   MSGL_CHECK(out && q && page_table && prefix_lens && extend_lens && q_offsets, MSGL_ERR_NULL,
              "out, q, page_table, prefix_lens, extend_lens and q_offsets must be non-NULL");

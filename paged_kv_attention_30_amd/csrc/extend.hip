@@ -205,7 +205,10 @@ paged_extend_kernel(ExtendParams p) {
   // of each tile.  Piece I holds keys 4I .. 4I+3; lane l of it lands on key
   // 4I + l/16 at physical 16-byte position l % 16, i.e. K chunk
   // (l%16) ^ (key & 15) and V 16-byte unit (l%16) ^ (4 * (key & 3)).
-  const int64_t cs = p.cache_stride_bytes;
+  // row offsets in 32 x 32 -> 64-bit arithmetic (the host checks that the
+  // row stride fits 32 bits); slots clamp to the pool
+  const uint32_t cs32 = (uint32_t)p.cache_stride_bytes;
+  const int slot_max = (int)min(p.num_slots - 1, (int64_t)INT32_MAX);
   const char* kbase = p.k_cache + (int64_t)g * kHeadDim * 2;
   const int64_t v_minus_k = p.v_cache - p.k_cache;
   const int ld_keyoff = lane >> 4;     // key within a piece
@@ -225,15 +228,15 @@ paged_extend_kernel(ExtendParams p) {
     const int32_t* rs = ring + (tile & (kPtRing - 1)) * kBN;
     // all table reads first: the loads below are opaque to the compiler,
     // so a read placed after one of them would wait for it
-    int64_t slot[kPPW];
+    int32_t slot[kPPW];
 #pragma unroll
     for (int u = 0; u < kPPW; ++u) slot[u] = rs[4 * (kPPW * w + u) + ld_keyoff];
 #pragma unroll
     for (int u = 0; u < kPPW; ++u) {
       const int piece = kPPW * w + u;
       const int key = 4 * piece + ld_keyoff;       // key within the tile
-      const int64_t sl = slot[u] < 0 ? 0 : (slot[u] >= p.num_slots ? p.num_slots - 1 : slot[u]);
-      const char* rowp = kbase + sl * cs;
+      const uint32_t sl = (uint32_t)min(max(slot[u], 0), slot_max);
+      const char* rowp = kbase + (uint64_t)sl * cs32;
       const int kchunk = ld_phys ^ (key & 15);
       const int vunit = ld_phys ^ (4 * (key & 3));
       dma16(rowp + 16 * kchunk, kd + piece * 512);
@@ -328,13 +331,11 @@ paged_extend_kernel(ExtendParams p) {
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const int i0 = 8 * (u & 1) + 2 * e2;
-        float p0 = fast_exp2(fmaf(s[u >> 1][i0], c, -m_run));
-        float p1 = fast_exp2(fmaf(s[u >> 1][i0 + 1], c, -m_run));
-        if (masked_tile) {
-          const int key0 = kt + 32 * (u >> 1) + 8 * (i0 >> 2) + 4 * jh + (i0 & 3);
-          p0 = key0 < vis_end ? p0 : 0.f;
-          p1 = key0 + 1 < vis_end ? p1 : 0.f;
-        }
+        // a masked score is +-inf with the sign that makes c * s = -inf, and
+        // m_run is finite here (key 0 is visible to every row, and c != 0),
+        // so a masked key's weight comes out exactly 0
+        const float p0 = fast_exp2(fmaf(s[u >> 1][i0], c, -m_run));
+        const float p1 = fast_exp2(fmaf(s[u >> 1][i0 + 1], c, -m_run));
         pb[u][e2] = pack_bf16x2(p0, p1);
         psum += p0 + p1;
       }
@@ -509,6 +510,10 @@ hipError_t launch_paged_extend(const ExtendArgs& a) {
   p.num_q_heads = a.num_q_heads;
   p.ratio = a.num_q_heads / a.num_kv_heads;
   p.scale_log2 = a.sm_scale * kLog2e;
+  // a zero scale (uniform weights) becomes the smallest normal float: the
+  // weights stay 2^0 = 1 to the last bit, and masked scores (-inf) still
+  // give -inf instead of inf * 0
+  if (p.scale_log2 == 0.f) p.scale_log2 = FLT_MIN;
   p.num_kv_heads = a.num_kv_heads;
   p.bq = extend_rows_per_block(p.ratio);
   p.n_qtiles = (a.max_extend_len + p.bq - 1) / p.bq;

@@ -350,6 +350,42 @@ def test_extend_planned_order_is_bitwise_the_natural_order():
     assert_lse_close(lp, rl, "extend planned lse")
 
 
+def test_extend_zero_scale_is_causal_mean_of_values():
+    # sm_scale = 0: every visible key weighs the same, so query i of a
+    # request with prefix P gets the mean of V over keys 0 .. P + i
+    banner("extend sm_scale=0")
+    inp = small_extend(93, 32, 8, [(70, 90), (0, 65)], num_slots=2048, sm_scale=0.0)
+    u = Uploaded(inp)
+    u.store()
+    out, lse = u.extend()
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    got = f64(out)
+    got_lse = lse.cpu().numpy()
+    for r in range(inp.num_extend):
+        P, E, base = int(inp.ext_prefix_lens[r]), int(inp.ext_extend_lens[r]), int(inp.ext_q_offsets[r])
+        slots = inp.page_table[inp.ext_req_rows[r], :P + E]
+        vrows = oracle.bf16_to_f64(vp[slots])                       # [P+E, Hkv, D]
+        cmean = np.cumsum(vrows, axis=0) / np.arange(1, P + E + 1)[:, None, None]
+        for i in (0, 1, E // 2, E - 1):
+            ref = np.repeat(cmean[P + i], 4, axis=0)
+            assert np.abs(got[base + i] - ref).max() <= 2e-2, (r, i)
+            assert np.allclose(got_lse[base + i], math.log(P + i + 1), atol=1e-4)
+
+
+def test_extend_negative_scale():
+    banner("extend sm_scale<0")
+    inp = small_extend(94, 16, 8, [(33, 70), (0, 40)], num_slots=2048, sm_scale=-0.09)
+    u = Uploaded(inp)
+    u.store()
+    out, lse = u.extend()
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle_extend(inp, kp, vp)
+    assert_close(out, ro, "extend negative scale")
+    assert_lse_close(lse, rl, "extend negative scale lse")
+
+
 def test_extend_with_shared_prefix_and_page_size_16():
     banner("extend shared prefix, page 16 vs 1")
     inp = small_extend(90, 32, 8, [(64, 100), (64, 37), (128, 64)], page_size=16,
