@@ -135,7 +135,9 @@ constexpr int kPPW = kPieces / kWaves;   // 1-KiB pieces each wave loads per K (
 // waves finish softmax and P V of tile k-1 and then compute S of tile k.
 // Each SIMD holds one wave of each group, so one wave's MFMA work runs
 // beside the other's softmax (exp and VALU) instead of both contending for
-// the same unit at the same time.
+// the same unit at the same time.  A wave raises its issue priority while it
+// issues MFMAs (S = K Q^T, O += P V) and drops it for the softmax, so the
+// SIMD feeds the matrix unit first and fills the gaps with vector work.
 __global__ void __launch_bounds__(kWaves * 64, 1)
 paged_extend_kernel(ExtendParams p) {
   // stage t % kStages holds the K and V of tile t
@@ -270,6 +272,7 @@ paged_extend_kernel(ExtendParams p) {
   // S^T for key blocks 0 and 1 of a tile
   f32x16 s[2];
   auto qk = [&](int tile) {
+    __builtin_amdgcn_s_setprio(1);
     const uint16_t* kt_lds = kbuf + (tile & (kStages - 1)) * kTileElems;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -288,6 +291,7 @@ paged_extend_kernel(ExtendParams p) {
   auto softmax_pv = [&](int tile) {
     const uint16_t* vt_lds = vbuf + (tile & (kStages - 1)) * kTileElems;
     const int kt = tile * kBN;
+    __builtin_amdgcn_s_setprio(0);
     // causal mask (only tiles that reach past some row's last visible key)
     const bool masked_tile = kt + kBN > vis_min;
     if (masked_tile) {
@@ -341,6 +345,7 @@ paged_extend_kernel(ExtendParams p) {
       }
     }
     l_run += psum;
+    __builtin_amdgcn_s_setprio(1);
 
     // O^T += V^T P^T: slot (jh, e) of step u is key 16u + 8(e/4) + 4jh + e%4
 #pragma unroll
@@ -354,6 +359,7 @@ paged_extend_kernel(ExtendParams p) {
         acc[mb] = mfma32x32x16(a, pb[u], acc[mb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   // Load schedule per wave (vector-memory loads complete in order):
