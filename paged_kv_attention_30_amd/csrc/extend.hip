@@ -9,14 +9,19 @@
 // back to back (cu_seqlens_q); §4.6.7 — the new K/V were stored before the
 // kernel.  Query i of a request with prefix P sees keys 0 .. P+i.
 //
-// gfx950 design: one workgroup of 4 waves takes one request, one kv head and
-// 128 query rows made of (q head of the group, query position) pairs, so the
+// gfx950 design.  A planning pass orders the (request, query tile) work
+// items longest first; the attention grid is 1-D with the kv head varying
+// fastest, so each XCD serves fixed kv heads and takes the longest items
+// first.  One workgroup of 8 waves takes one request, one kv head and 256
+// query rows made of (q head of the group, query position) pairs, so the
 // K/V tiles staged in LDS serve the whole GQA group.  Per 64-key tile:
 // * K and V go from HBM straight into LDS (global_load_lds_dwordx4: each
-//   wave instruction fills 1 KiB of LDS, lane l at +16 l), two stages deep,
-//   one barrier per tile; no register staging.  Which key / 16-byte piece a
-//   lane fetches is chosen so the LDS tiles come out XOR-swizzled for
-//   conflict-free operand reads.
+//   wave instruction fills 1 KiB of LDS, lane l at +16 l), issued from
+//   inline assembly two tiles ahead into four stages, with explicit vmcnt
+//   waits and one barrier per tile; no register staging.  Which key /
+//   16-byte piece a lane fetches is chosen so the LDS tiles come out
+//   XOR-swizzled for conflict-free operand reads.  The page-table entries
+//   arrive the same way, into a small per-wave ring.
 // * S^T = K Q^T on the 32x32x16 bf16 MFMA (A = K rows read from LDS, B = q
 //   rows held in registers).
 // * online softmax per query row (every lane owns one row); the reference
