@@ -8,10 +8,12 @@ produced by the ``workloads`` package.
 
 Everything here is written from the definitions on the source pages
 (cited per function) and computes in float64 after an exact bf16 -> f64
-upcast.  See ``oracle/attention.py`` for the functions and their pins
-(the ``tests/test_oracle_*.py`` files); every function is pinned.
+upcast.  See ``oracle/attention.py`` and ``oracle/embedding.py`` for the
+functions and their pins (the ``tests/test_oracle_*.py`` files); every
+function is pinned.
 """
 
+from .embedding import embedding_gather  # noqa: F401
 from .attention import (  # noqa: F401
     bf16_to_f64,
     f64_to_bf16_rne,
