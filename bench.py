@@ -47,6 +47,9 @@ WORKLOAD_TEXT = {
            "(lens U[256,8192]) + extend (prefix 6144, extend 2048); 64 requests share a "
            "1,024-token prefix; Hq 32 / Hkv 8, seed 5",
     "C5b": "mixed batch as C5a at page_size 16 (16-slot pages, page permutation), seed 5",
+    "EMB": "embedding gather: 8,192 token ids uniform over a 151,936 x 4,096 bf16 table "
+           "(Qwen3-8B-class vocabulary and hidden size, one tensor-parallel rank), ids int32, "
+           "table N(0,1), seed 41",
 }
 
 
@@ -297,6 +300,35 @@ def cpu_baseline(inp, budget_s: float = 12.0):
                       f"{os.cpu_count()} logical CPUs visible"}
 
 
+def embedding_run(steps: int, warmup: int):
+    """Time back-to-back planned embedding gathers (HBM-bound row copy)."""
+    import torch
+    import paged_kv_attention_30_amd as msgl
+    g = torch.Generator(device="cuda").manual_seed(41)
+    V, H, n = 151936, 4096, 8192
+    table = torch.randn((V, H), generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+    ids = torch.randint(0, V, (n,), generator=g, device="cuda", dtype=torch.int32)
+    out = torch.empty((n, H), dtype=torch.bfloat16, device="cuda")
+    plan = msgl.plan_embedding_gather(table, ids, out=out)
+    for _ in range(warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        plan.run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    alg = n * H * 2 * 2 + n * 4           # rows read + rows written + ids
+    del table, out
+    return {"workload": WORKLOAD_TEXT["EMB"], "gather_ms": round(ms, 4),
+            "alg_bytes": alg, "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(n / (ms * 1e-3), 1)}
+
+
 def decode_figures(inp, res, steps):
     from workloads import metrics
     kv = metrics.decode_kv_bytes(inp.page_table, inp.dec_req_rows, inp.dec_seq_lens,
@@ -342,7 +374,8 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--configs", default="C3", help="extra workloads (comma list of C3,C4,C5a,C5b; '' for none)")
+    ap.add_argument("--configs", default="C3,EMB",
+                    help="extra workloads (comma list of C3,C4,C5a,C5b,EMB; '' for none)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
@@ -378,6 +411,9 @@ def main(argv=None) -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         log(f"copied {args.calibrate_copy} MiB three times")
+    if args.only == "EMB":
+        print(json.dumps({"only": "EMB", **embedding_run(args.steps, args.warmup)}))
+        return 0
     if args.only:
         inp_o = make_config(args.only)
         run_o = Run(inp_o, args.split_tokens)
@@ -411,6 +447,10 @@ def main(argv=None) -> int:
     extras = {"C2": head}
     for name in [c for c in args.configs.split(",") if c]:
         log(f"workload {name}")
+        if name == "EMB":
+            extras[name] = embedding_run(max(10, args.steps // 2), 3)
+            torch.cuda.empty_cache()
+            continue
         inp_x = make_config(name)
         run_x = Run(inp_x, args.split_tokens)
         res_x = timed_steps(run_x, max(5, args.steps // 5), 3, args.graphs)

@@ -22,6 +22,10 @@
  *                      pages do not describe split-KV; the merge is the exact
  *                      identity that recombines a softmax split over disjoint
  *                      key sets)
+ *   msgl_embedding_gather  token-id -> embedding-row gather with the
+ *                      vocabulary-shard mask ["Mini-SGLang complete analysis",
+ *                      §4.9.3 (indexing), §4.7.8 (embed_tokens sharded along
+ *                      the vocabulary, masked indexing + all-reduce)]
  *
  * Conventions shared by every call
  * --------------------------------
@@ -184,6 +188,29 @@ int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_st
 size_t msgl_paged_extend_workspace_size(int32_t batch, int32_t num_q_heads,
                                         int32_t num_kv_heads, int32_t head_dim,
                                         int32_t max_extend_len, int32_t max_kv_len);
+
+/*
+ * msgl_embedding_gather — vocabulary-sharded embedding lookup ("Mini-SGLang
+ * complete analysis" §4.9.3: one indexing(weights, ids, vocab_range) call
+ * copies one table row per token id; §4.7.8: embed_tokens is split along the
+ * vocabulary across tensor-parallel ranks and combined by masked indexing
+ * plus an all-reduce).  For i < n:
+ *   out[i] = weights[ids[i] - vocab_start]   if 0 <= ids[i] - vocab_start < num_rows
+ *   out[i] = 0                               otherwise
+ * Rows are copied bit for bit.
+ *
+ *   out        [n, hidden] elements, row i at i * out_row_stride
+ *   weights    this shard's table, [num_rows, hidden], row r at
+ *              r * weight_row_stride (strides in elements, >= hidden)
+ *   ids        n token ids, int32 (MSGL_INDEX_I32) or int64 (MSGL_INDEX_I64)
+ *   dtype      MSGL_DTYPE_BF16 or MSGL_DTYPE_F32 (element size 2 or 4)
+ * Pointers must be aligned to their element size.  n == 0 is a no-op.
+ * Enqueues on `stream`; the caller owns every buffer.
+ */
+int msgl_embedding_gather(void* out, int64_t out_row_stride, const void* weights,
+                          int64_t num_rows, int64_t weight_row_stride, const void* ids,
+                          int32_t index_dtype, int64_t n, int64_t vocab_start, int32_t hidden,
+                          int32_t dtype, hipStream_t stream);
 
 /*
  * msgl_merge_states — for each (n, h): M = max_s part_lse[s, n, h],

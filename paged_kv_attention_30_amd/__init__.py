@@ -18,6 +18,8 @@ from .binding import (  # noqa: F401
     paged_extend,
     paged_extend_workspace_size,
     merge_states,
+    embedding_gather,
+    plan_embedding_gather,
     alloc_workspace,
 )
 from ._build import LIB_PATH  # noqa: F401

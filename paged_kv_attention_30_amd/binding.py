@@ -49,6 +49,8 @@ SIGNATURES = {
     "msgl_paged_extend_workspace_size": (_size_t, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "msgl_merge_states": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i32,
                                  _i32, _i32, _c_void_p]),
+    "msgl_embedding_gather": (_i32, [_c_void_p, _i64, _c_void_p, _i64, _i64, _c_void_p, _i32,
+                                     _i64, _i64, _i32, _i32, _c_void_p]),
 }
 
 
@@ -375,3 +377,37 @@ def merge_states(part_out: torch.Tensor, part_lse: torch.Tensor,
                                code, _stream(stream))
     _check(st, "msgl_merge_states")
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# embedding gather
+# ---------------------------------------------------------------------------
+
+def plan_embedding_gather(weights: torch.Tensor, ids: torch.Tensor, vocab_start: int = 0,
+                          out: torch.Tensor | None = None) -> PlannedCall:
+    """Planned form of :func:`embedding_gather`; ``run()`` returns ``out``."""
+    lib = load()
+    if weights.dim() != 2 or weights.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("weights must be a [rows, hidden] bf16 or fp32 tensor")
+    if not weights.is_cuda or weights.stride(1) != 1:
+        raise ValueError("weights must be a GPU tensor with contiguous rows")
+    if ids.dim() != 1 or ids.dtype not in (torch.int32, torch.int64) or not ids.is_contiguous() \
+            or not ids.is_cuda:
+        raise TypeError("ids must be a contiguous [n] int32 / int64 GPU tensor")
+    rows, hidden = weights.shape
+    n = ids.shape[0]
+    if out is None:
+        out = torch.empty((n, hidden), dtype=weights.dtype, device=weights.device)
+    if out.dtype != weights.dtype or tuple(out.shape) != (n, hidden) or out.stride(1) != 1:
+        raise ValueError("out must be [n, hidden] of the table's dtype with contiguous rows")
+    args = (_ptr(out), out.stride(0), _ptr(weights), rows, weights.stride(0), _ptr(ids),
+            INDEX_I64 if ids.dtype == torch.int64 else INDEX_I32, n, int(vocab_start), hidden,
+            DTYPE_BF16 if weights.dtype == torch.bfloat16 else DTYPE_F32)
+    return PlannedCall(lib.msgl_embedding_gather, args, "msgl_embedding_gather", out,
+                       (weights, ids))
+
+
+def embedding_gather(weights: torch.Tensor, ids: torch.Tensor, vocab_start: int = 0,
+                     out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """out[i] = weights[ids[i] - vocab_start], zeros for ids outside this shard."""
+    return plan_embedding_gather(weights, ids, vocab_start, out).run(stream)

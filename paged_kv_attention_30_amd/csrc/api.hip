@@ -344,6 +344,54 @@ int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_st
   return launch_status(msgl::launch_paged_extend(a), "paged_extend");
 }
 
+int msgl_embedding_gather(void* out, int64_t out_row_stride, const void* weights,
+                          int64_t num_rows, int64_t weight_row_stride, const void* ids,
+                          int32_t index_dtype, int64_t n, int64_t vocab_start, int32_t hidden,
+                          int32_t dtype, hipStream_t stream) {
+  g_last_error[0] = 0;
+  MSGL_CHECK(n >= 0, MSGL_ERR_SHAPE, "n %lld is negative", (long long)n);
+  MSGL_CHECK(num_rows >= 0, MSGL_ERR_SHAPE, "num_rows %lld is negative", (long long)num_rows);
+  MSGL_CHECK(hidden > 0, MSGL_ERR_SHAPE, "hidden %d must be positive", hidden);
+  MSGL_CHECK(dtype == MSGL_DTYPE_BF16 || dtype == MSGL_DTYPE_F32, MSGL_ERR_UNSUPPORTED,
+             "dtype %d unsupported", dtype);
+  MSGL_CHECK(index_dtype == MSGL_INDEX_I32 || index_dtype == MSGL_INDEX_I64, MSGL_ERR_UNSUPPORTED,
+             "index dtype %d unsupported", index_dtype);
+  MSGL_CHECK(out_row_stride >= hidden && weight_row_stride >= hidden, MSGL_ERR_SHAPE,
+             "row strides (%lld, %lld) must be >= hidden %d", (long long)out_row_stride,
+             (long long)weight_row_stride, hidden);
+  if (n == 0) return MSGL_OK;
+  MSGL_CHECK(out && ids && (weights || num_rows == 0), MSGL_ERR_NULL,
+             "out, ids and weights must be non-NULL");
+  const int esz = dtype == MSGL_DTYPE_BF16 ? 2 : 4;
+  MSGL_CHECK(aligned(out, esz) && aligned(weights, esz), MSGL_ERR_ALIGN,
+             "out and weights must be aligned to their element size");
+  MSGL_CHECK(aligned(ids, index_dtype == MSGL_INDEX_I64 ? 8 : 4), MSGL_ERR_ALIGN,
+             "ids must be aligned to their element size");
+
+  msgl::GatherArgs a;
+  a.out = out;
+  a.out_stride_bytes = out_row_stride * esz;
+  a.weights = weights;
+  a.w_stride_bytes = weight_row_stride * esz;
+  a.rows = num_rows;
+  a.vocab_start = vocab_start;
+  a.ids = ids;
+  a.index_is_i64 = index_dtype == MSGL_INDEX_I64;
+  a.n = n;
+  a.row_bytes = (int64_t)hidden * esz;
+  a.stream = stream;
+  int unit = 16;
+  while (unit > esz) {
+    const bool ok = aligned(out, unit) && aligned(weights, unit) &&
+                    a.out_stride_bytes % unit == 0 && a.w_stride_bytes % unit == 0 &&
+                    a.row_bytes % unit == 0;
+    if (ok) break;
+    unit /= 2;
+  }
+  a.unit_bytes = unit;
+  return launch_status(msgl::launch_embedding_gather(a), "embedding_gather");
+}
+
 int msgl_merge_states(void* out, float* lse_out, const float* part_out, const float* part_lse,
                       int32_t num_parts, int64_t n, int32_t num_heads, int32_t head_dim,
                       int32_t out_dtype, hipStream_t stream) {

@@ -28,6 +28,21 @@ struct StoreArgs {
   hipStream_t stream;
 };
 
+struct GatherArgs {
+  void* out;
+  int64_t out_stride_bytes;
+  const void* weights;
+  int64_t w_stride_bytes;
+  int64_t rows;            // table rows this shard holds
+  int64_t vocab_start;     // vocabulary id of the shard's row 0
+  const void* ids;
+  bool index_is_i64;
+  int64_t n;
+  int64_t row_bytes;
+  int unit_bytes;          // 16, 8, 4 or 2: widest unit every address is aligned to
+  hipStream_t stream;
+};
+
 struct DecodeArgs {
   void* out;               // bf16 [B, Hq, 128]
   float* lse;              // fp32 [B, Hq] or null
@@ -109,6 +124,7 @@ constexpr int kMaxDecodeBlocks = 2048;
 
 int decode_kv_heads_per_block(int num_kv_heads);
 hipError_t launch_store_kv(const StoreArgs& a);
+hipError_t launch_embedding_gather(const GatherArgs& a);
 hipError_t launch_paged_decode(const DecodeArgs& a);
 hipError_t launch_paged_extend(const ExtendArgs& a);
 hipError_t launch_merge(const MergeArgs& a);

@@ -200,3 +200,25 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         binding.load(str(tmp_path / "nope.so"))
     monkeypatch.setattr(binding, "_lib", None)
     binding.load()
+
+
+def test_embedding_gather_validation(lib):
+    def gather(**kw):
+        a = dict(out=FAKE, ostride=64, w=FAKE2, rows=100, wstride=64, ids=FAKE, idx=0, n=8,
+                 start=0, hidden=64, dtype=0)
+        a.update(kw)
+        return lib.msgl_embedding_gather(a["out"], a["ostride"], a["w"], a["rows"], a["wstride"],
+                                         a["ids"], a["idx"], a["n"], a["start"], a["hidden"],
+                                         a["dtype"], None)
+    assert gather(n=0) == OK
+    assert gather(n=-1) == SHAPE
+    assert gather(rows=-1) == SHAPE
+    assert gather(hidden=0) == SHAPE
+    assert gather(ostride=32) == SHAPE
+    assert gather(wstride=10) == SHAPE
+    assert gather(dtype=3) == UNSUP
+    assert gather(idx=2) == UNSUP
+    assert gather(ids=None) == NULL
+    assert gather(w=None) == NULL
+    assert gather(out=FAKE + 1) == ALIGN
+    assert gather(idx=1, ids=FAKE + 4) == ALIGN
