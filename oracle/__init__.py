@@ -8,12 +8,14 @@ produced by the ``workloads`` package.
 
 Everything here is written from the definitions on the source pages
 (cited per function) and computes in float64 after an exact bf16 -> f64
-upcast.  See ``oracle/attention.py`` and ``oracle/embedding.py`` for the
+upcast.  See ``oracle/attention.py``, ``oracle/embedding.py`` and
+``oracle/prologue.py`` for the
 functions and their pins (the ``tests/test_oracle_*.py`` files); every
 function is pinned.
 """
 
 from .embedding import embedding_gather  # noqa: F401
+from .prologue import rope_cache, rms_norm, rope, qk_norm_rope_store  # noqa: F401
 from .attention import (  # noqa: F401
     bf16_to_f64,
     f64_to_bf16_rne,
