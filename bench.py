@@ -47,6 +47,10 @@ WORKLOAD_TEXT = {
            "(lens U[256,8192]) + extend (prefix 6144, extend 2048); 64 requests share a "
            "1,024-token prefix; Hq 32 / Hkv 8, seed 5",
     "C5b": "mixed batch as C5a at page_size 16 (16-slot pages, page permutation), seed 5",
+    "PRO": "attention-layer prologue (q/k RMSNorm + RoPE + store_kv): a chunk of 8,192 tokens at "
+           "positions 0..8191, Hq 32 / Hkv 8 / D 128 (Qwen3-8B-class), merged qkv bf16 N(0,1), "
+           "norm weights N(0,1), RoPE base 1e6, slots a random permutation of a 524,288-slot pool, "
+           "seed 42",
     "EMB": "embedding gather: 8,192 token ids uniform over a 151,936 x 4,096 bf16 table "
            "(Qwen3-8B-class vocabulary and hidden size, one tensor-parallel rank), ids int32, "
            "table N(0,1), seed 41",
@@ -329,6 +333,42 @@ def embedding_run(steps: int, warmup: int):
             "tokens_per_s": round(n / (ms * 1e-3), 1)}
 
 
+def prologue_run(steps: int, warmup: int):
+    """Time back-to-back fused prologues (q/k RMSNorm + RoPE + store; HBM-bound)."""
+    import torch
+    import paged_kv_attention_30_amd as msgl
+    g = torch.Generator(device="cuda").manual_seed(42)
+    T, Hq, Hkv, D, S = 8192, 32, 8, 128, 524288
+    qkv = torch.randn((T, (Hq + 2 * Hkv) * D), generator=g, device="cuda").to(torch.bfloat16)
+    k = torch.empty((S, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty_like(k)
+    qw = torch.randn((D,), generator=g, device="cuda").to(torch.bfloat16)
+    kw = torch.randn((D,), generator=g, device="cuda").to(torch.bfloat16)
+    pos = torch.arange(T, dtype=torch.int32, device="cuda")
+    loc = torch.randperm(S, generator=g, device="cuda")[:T].to(torch.int32)
+    cache = msgl.rope_cos_sin_cache(32768, D, 1_000_000.0)
+    q_out = torch.empty((T, Hq, D), dtype=torch.bfloat16, device="cuda")
+    plan = msgl.plan_qk_norm_rope_store(qkv, k, v, pos, cache, loc, Hq, Hkv, qw, kw, 1e-6, q_out)
+    for _ in range(warmup):
+        plan.run()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        plan.run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    # qkv rows in; q out, k and v rows to the pool; positions, slots, table rows
+    alg = T * (Hq + 2 * Hkv) * D * 2 + T * (Hq + 2 * Hkv) * D * 2 + T * 4 * 2 + T * D * 4
+    del qkv, k, v, q_out
+    return {"workload": WORKLOAD_TEXT["PRO"], "prologue_ms": round(ms, 4), "alg_bytes": alg,
+            "GBps": round(alg / (ms * 1e-3) / 1e9, 1),
+            "hbm_frac": round(alg / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "tokens_per_s": round(T / (ms * 1e-3), 1)}
+
+
 def decode_figures(inp, res, steps):
     from workloads import metrics
     kv = metrics.decode_kv_bytes(inp.page_table, inp.dec_req_rows, inp.dec_seq_lens,
@@ -374,8 +414,8 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--configs", default="C3,EMB",
-                    help="extra workloads (comma list of C3,C4,C5a,C5b,EMB; '' for none)")
+    ap.add_argument("--configs", default="C3,EMB,PRO",
+                    help="extra workloads (comma list of C3,C4,C5a,C5b,EMB,PRO; '' for none)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
@@ -414,6 +454,9 @@ def main(argv=None) -> int:
     if args.only == "EMB":
         print(json.dumps({"only": "EMB", **embedding_run(args.steps, args.warmup)}))
         return 0
+    if args.only == "PRO":
+        print(json.dumps({"only": "PRO", **prologue_run(args.steps, args.warmup)}))
+        return 0
     if args.only:
         inp_o = make_config(args.only)
         run_o = Run(inp_o, args.split_tokens)
@@ -447,8 +490,9 @@ def main(argv=None) -> int:
     extras = {"C2": head}
     for name in [c for c in args.configs.split(",") if c]:
         log(f"workload {name}")
-        if name == "EMB":
-            extras[name] = embedding_run(max(10, args.steps // 2), 3)
+        if name in ("EMB", "PRO"):
+            fn = embedding_run if name == "EMB" else prologue_run
+            extras[name] = fn(max(10, args.steps // 2), 3)
             torch.cuda.empty_cache()
             continue
         inp_x = make_config(name)

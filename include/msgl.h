@@ -22,6 +22,9 @@
  *                      pages do not describe split-KV; the merge is the exact
  *                      identity that recombines a softmax split over disjoint
  *                      key sets)
+ *   msgl_rope_cos_sin_cache, msgl_qk_norm_rope_store   the attention layer's
+ *                      prologue: q/k RMSNorm, RoPE, store of K/V, fused
+ *                      ["Mini-SGLang complete analysis" §4.6.7, §4.5.6]
  *   msgl_embedding_gather  token-id -> embedding-row gather with the
  *                      vocabulary-shard mask ["Mini-SGLang complete analysis",
  *                      §4.9.3 (indexing), §4.7.8 (embed_tokens sharded along
@@ -211,6 +214,54 @@ int msgl_embedding_gather(void* out, int64_t out_row_stride, const void* weights
                           int64_t num_rows, int64_t weight_row_stride, const void* ids,
                           int32_t index_dtype, int64_t n, int64_t vocab_start, int32_t hidden,
                           int32_t dtype, hipStream_t stream);
+
+/*
+ * msgl_rope_cos_sin_cache — the RoPE table shared by every layer ("Mini-SGLang
+ * complete analysis" §4.5.6: one cos/sin cache of max_position x rotary_dim).
+ * Row p of `cache` ([max_position, rotary_dim] fp32, caller-owned) receives
+ * cos(p * theta_i) in columns [0, rotary_dim/2) and sin(p * theta_i) in
+ * [rotary_dim/2, rotary_dim), theta_i = base^(-2i / rotary_dim); angle and
+ * functions in double precision, rounded to fp32 once.  rotary_dim must be
+ * positive and even.
+ */
+int msgl_rope_cos_sin_cache(float* cache, int64_t max_position, int32_t rotary_dim, double base,
+                            hipStream_t stream);
+
+/*
+ * msgl_qk_norm_rope_store — the attention layer's prologue, fused ("Mini-SGLang
+ * complete analysis" §4.6.7: split the merged qkv into q, k, v; RMS-normalise
+ * q and k per head (Qwen3's q_norm / k_norm); rotate q and k with RoPE at the
+ * batch positions; store k and v into the paged pool at out_loc).  For token t
+ * and head vector x (128 dims):
+ *   norm(x) = x / sqrt(mean(x^2) + eps) * w      (skipped when w is NULL)
+ *   rope(x)[i]      = x[i] cos(p t_i) - x[i+64] sin(p t_i)      i < 64
+ *   rope(x)[i + 64] = x[i+64] cos(p t_i) + x[i] sin(p t_i)      (rotate half)
+ * with cos / sin read from `cos_sin_cache` row p = positions[t] (clamped to
+ * [0, max_position)).  Outputs, rounded to bf16 once:
+ *   q_out[t, h]              = rope(norm_q(q[t, h]))
+ *   k_cache[out_loc[t], g]   = rope(norm_k(k[t, g]))
+ *   v_cache[out_loc[t], g]   = v[t, g]                 (bit copy)
+ *
+ *   qkv        bf16 [n, (Hq + 2 Hkv) * 128]: q heads, then k heads, then v
+ *              heads; row t at t * qkv_row_stride elements
+ *   q_out      bf16 [n, Hq, 128], row t at t * q_out_row_stride; may be the
+ *              qkv buffer itself (q_out = qkv, same stride) for in-place use
+ *   k_cache, v_cache, num_slots, cache_row_stride   as for msgl_store_kv
+ *   q_norm_weight, k_norm_weight   bf16 [128] each, or NULL
+ *   positions  int32 [n];  cos_sin_cache  fp32 [max_position, 128] as built by
+ *              msgl_rope_cos_sin_cache
+ *   out_loc    n distinct slots, int32 or int64 (index_dtype); not checked
+ * head_dim must be 128, num_q_heads a multiple of num_kv_heads; rows, norm
+ * weights and the table 16-byte aligned, row strides multiples of 8 elements.
+ * n == 0 is a no-op.
+ */
+int msgl_qk_norm_rope_store(void* q_out, int64_t q_out_row_stride, void* k_cache, void* v_cache,
+                            int64_t num_slots, int64_t cache_row_stride, const void* qkv,
+                            int64_t qkv_row_stride, const void* q_norm_weight,
+                            const void* k_norm_weight, float eps, const int32_t* positions,
+                            const float* cos_sin_cache, int64_t max_position, const void* out_loc,
+                            int32_t index_dtype, int64_t n, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, hipStream_t stream);
 
 /*
  * msgl_merge_states — for each (n, h): M = max_s part_lse[s, n, h],

@@ -19,6 +19,9 @@ from .binding import (  # noqa: F401
     paged_extend_workspace_size,
     merge_states,
     embedding_gather,
+    rope_cos_sin_cache,
+    qk_norm_rope_store,
+    plan_qk_norm_rope_store,
     plan_embedding_gather,
     alloc_workspace,
 )

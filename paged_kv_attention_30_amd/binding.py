@@ -51,6 +51,11 @@ SIGNATURES = {
                                  _i32, _i32, _c_void_p]),
     "msgl_embedding_gather": (_i32, [_c_void_p, _i64, _c_void_p, _i64, _i64, _c_void_p, _i32,
                                      _i64, _i64, _i32, _i32, _c_void_p]),
+    "msgl_rope_cos_sin_cache": (_i32, [_c_void_p, _i64, _i32, ctypes.c_double, _c_void_p]),
+    "msgl_qk_norm_rope_store": (_i32, [_c_void_p, _i64, _c_void_p, _c_void_p, _i64, _i64,
+                                       _c_void_p, _i64, _c_void_p, _c_void_p, _f32, _c_void_p,
+                                       _c_void_p, _i64, _c_void_p, _i32, _i64, _i32, _i32, _i32,
+                                       _c_void_p]),
 }
 
 
@@ -411,3 +416,71 @@ def embedding_gather(weights: torch.Tensor, ids: torch.Tensor, vocab_start: int 
                      out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """out[i] = weights[ids[i] - vocab_start], zeros for ids outside this shard."""
     return plan_embedding_gather(weights, ids, vocab_start, out).run(stream)
+
+
+# ---------------------------------------------------------------------------
+# attention-layer prologue: q/k RMSNorm + RoPE + store
+# ---------------------------------------------------------------------------
+
+def rope_cos_sin_cache(max_position: int, rotary_dim: int = 128, base: float = 1_000_000.0,
+                       device=None, stream=None) -> torch.Tensor:
+    """fp32 [max_position, rotary_dim] table: cos | sin of p * base^(-2i/rotary_dim)."""
+    lib = load()
+    cache = torch.empty((max_position, rotary_dim), dtype=torch.float32, device=device or "cuda")
+    st = lib.msgl_rope_cos_sin_cache(_ptr(cache), max_position, rotary_dim, float(base),
+                                     _stream(stream))
+    _check(st, "msgl_rope_cos_sin_cache")
+    return cache
+
+
+def plan_qk_norm_rope_store(qkv: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            positions: torch.Tensor, cos_sin_cache: torch.Tensor,
+                            out_loc: torch.Tensor, num_q_heads: int, num_kv_heads: int,
+                            q_norm_weight: torch.Tensor | None = None,
+                            k_norm_weight: torch.Tensor | None = None, eps: float = 1e-6,
+                            q_out: torch.Tensor | None = None) -> PlannedCall:
+    """Planned form of :func:`qk_norm_rope_store`; ``run()`` returns ``q_out``."""
+    lib = load()
+    n_slots, hkv, d, cstride = _pool_geometry(k_cache, v_cache)
+    _need(qkv, torch.bfloat16, "qkv", 2)
+    if hkv != num_kv_heads or qkv.shape[1] != (num_q_heads + 2 * num_kv_heads) * d \
+            or qkv.stride(1) != 1:
+        raise ValueError("qkv must be [n, (Hq + 2 Hkv) * D] with contiguous rows")
+    n = qkv.shape[0]
+    _need(positions, torch.int32, "positions", 1)
+    _need(cos_sin_cache, torch.float32, "cos_sin_cache", 2)
+    if positions.shape[0] != n or not positions.is_contiguous():
+        raise ValueError("positions must be a contiguous [n] vector")
+    if cos_sin_cache.shape[1] != d or not cos_sin_cache.is_contiguous():
+        raise ValueError("cos_sin_cache must be a contiguous [max_position, D] table")
+    if out_loc.dim() != 1 or out_loc.shape[0] != n or out_loc.dtype not in (torch.int32, torch.int64) \
+            or not out_loc.is_contiguous():
+        raise ValueError("out_loc must be a contiguous [n] int32 / int64 vector")
+    for name, w in (("q_norm_weight", q_norm_weight), ("k_norm_weight", k_norm_weight)):
+        if w is not None:
+            _need(w, torch.bfloat16, name, 1)
+            if w.shape[0] != d or not w.is_contiguous():
+                raise ValueError(f"{name} must be a contiguous [D] vector")
+    if q_out is None:
+        q_out = torch.empty((n, num_q_heads, d), dtype=torch.bfloat16, device=qkv.device)
+    q_stride = q_out.stride(0)
+    if q_out.dtype != torch.bfloat16 or q_out.shape[0] != n or q_out.stride(-1) != 1:
+        raise ValueError("q_out must be bf16 [n, Hq, D] (or the qkv buffer itself)")
+    args = (_ptr(q_out), q_stride, _ptr(k_cache), _ptr(v_cache), n_slots, cstride, _ptr(qkv),
+            qkv.stride(0), _ptr(q_norm_weight), _ptr(k_norm_weight), float(eps), _ptr(positions),
+            _ptr(cos_sin_cache), cos_sin_cache.shape[0], _ptr(out_loc),
+            INDEX_I64 if out_loc.dtype == torch.int64 else INDEX_I32, n, num_q_heads,
+            num_kv_heads, d)
+    return PlannedCall(lib.msgl_qk_norm_rope_store, args, "msgl_qk_norm_rope_store", q_out,
+                       (qkv, k_cache, v_cache, positions, cos_sin_cache, out_loc, q_norm_weight,
+                        k_norm_weight))
+
+
+def qk_norm_rope_store(qkv, k_cache, v_cache, positions, cos_sin_cache, out_loc, num_q_heads,
+                       num_kv_heads, q_norm_weight=None, k_norm_weight=None, eps=1e-6,
+                       q_out=None, stream=None) -> torch.Tensor:
+    """q/k RMSNorm + RoPE of one layer's merged qkv; stores k, v into the pool at out_loc
+    and returns the rotated q ([n, Hq, D] bf16, or ``q_out``)."""
+    return plan_qk_norm_rope_store(qkv, k_cache, v_cache, positions, cos_sin_cache, out_loc,
+                                   num_q_heads, num_kv_heads, q_norm_weight, k_norm_weight, eps,
+                                   q_out).run(stream)

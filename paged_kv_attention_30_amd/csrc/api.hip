@@ -392,6 +392,78 @@ int msgl_embedding_gather(void* out, int64_t out_row_stride, const void* weights
   return launch_status(msgl::launch_embedding_gather(a), "embedding_gather");
 }
 
+int msgl_rope_cos_sin_cache(float* cache, int64_t max_position, int32_t rotary_dim, double base,
+                            hipStream_t stream) {
+  g_last_error[0] = 0;
+  MSGL_CHECK(max_position >= 0, MSGL_ERR_SHAPE, "max_position %lld is negative",
+             (long long)max_position);
+  MSGL_CHECK(rotary_dim > 0 && rotary_dim % 2 == 0, MSGL_ERR_SHAPE,
+             "rotary_dim %d must be positive and even", rotary_dim);
+  MSGL_CHECK(base > 0.0, MSGL_ERR_SHAPE, "base must be positive");
+  if (max_position == 0) return MSGL_OK;
+  MSGL_CHECK(cache, MSGL_ERR_NULL, "cache must be non-NULL");
+  MSGL_CHECK(aligned(cache, 4), MSGL_ERR_ALIGN, "cache must be 4-byte aligned");
+  return launch_status(msgl::launch_rope_cache(cache, max_position, rotary_dim, base, stream),
+                       "rope_cos_sin_cache");
+}
+
+int msgl_qk_norm_rope_store(void* q_out, int64_t q_out_row_stride, void* k_cache, void* v_cache,
+                            int64_t num_slots, int64_t cache_row_stride, const void* qkv,
+                            int64_t qkv_row_stride, const void* q_norm_weight,
+                            const void* k_norm_weight, float eps, const int32_t* positions,
+                            const float* cos_sin_cache, int64_t max_position, const void* out_loc,
+                            int32_t index_dtype, int64_t n, int32_t num_q_heads,
+                            int32_t num_kv_heads, int32_t head_dim, hipStream_t stream) {
+  g_last_error[0] = 0;
+  MSGL_CHECK(n >= 0, MSGL_ERR_SHAPE, "n %lld is negative", (long long)n);
+  MSGL_CHECK(index_dtype == MSGL_INDEX_I32 || index_dtype == MSGL_INDEX_I64, MSGL_ERR_UNSUPPORTED,
+             "index dtype %d unsupported", index_dtype);
+  int st = validate_pool(k_cache, v_cache, num_slots, cache_row_stride, num_kv_heads, head_dim);
+  if (st) return st;
+  MSGL_CHECK(ratio_ok(num_q_heads, num_kv_heads), MSGL_ERR_UNSUPPORTED,
+             "num_q_heads %d / num_kv_heads %d: ratio must be 1, 2, 4, 8 or 16", num_q_heads,
+             num_kv_heads);
+  MSGL_CHECK(qkv_row_stride >= (int64_t)(num_q_heads + 2 * num_kv_heads) * head_dim, MSGL_ERR_SHAPE,
+             "qkv_row_stride %lld < (Hq + 2 Hkv) * head_dim", (long long)qkv_row_stride);
+  MSGL_CHECK(q_out_row_stride >= (int64_t)num_q_heads * head_dim, MSGL_ERR_SHAPE,
+             "q_out_row_stride %lld < Hq * head_dim", (long long)q_out_row_stride);
+  MSGL_CHECK(max_position > 0, MSGL_ERR_SHAPE, "max_position must be positive");
+  MSGL_CHECK(eps >= 0.f, MSGL_ERR_SHAPE, "eps must be non-negative");
+  if (n == 0) return MSGL_OK;
+  MSGL_CHECK(q_out && qkv && positions && cos_sin_cache && out_loc, MSGL_ERR_NULL,
+             "q_out, qkv, positions, cos_sin_cache and out_loc must be non-NULL");
+  MSGL_CHECK(aligned(q_out, 16) && aligned(qkv, 16) &&
+                 (!q_norm_weight || aligned(q_norm_weight, 16)) &&
+                 (!k_norm_weight || aligned(k_norm_weight, 16)) && aligned(positions, 4) &&
+                 aligned(cos_sin_cache, 16) &&
+                 aligned(out_loc, index_dtype == MSGL_INDEX_I64 ? 8 : 4),
+             MSGL_ERR_ALIGN, "rows, weights and table 16-byte aligned, indices element aligned");
+  MSGL_CHECK(qkv_row_stride % 8 == 0 && q_out_row_stride % 8 == 0, MSGL_ERR_ALIGN,
+             "qkv and q_out row strides must be multiples of 8 elements (16 bytes)");
+
+  msgl::PrologueArgs a;
+  a.q_out = q_out;
+  a.q_out_stride = q_out_row_stride;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.cache_stride = cache_row_stride;
+  a.qkv = qkv;
+  a.qkv_stride = qkv_row_stride;
+  a.q_norm_w = q_norm_weight;
+  a.k_norm_w = k_norm_weight;
+  a.eps = eps;
+  a.positions = positions;
+  a.cache = cos_sin_cache;
+  a.max_position = max_position;
+  a.out_loc = out_loc;
+  a.index_is_i64 = index_dtype == MSGL_INDEX_I64;
+  a.n = n;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = num_kv_heads;
+  a.stream = stream;
+  return launch_status(msgl::launch_qk_norm_rope_store(a), "qk_norm_rope_store");
+}
+
 int msgl_merge_states(void* out, float* lse_out, const float* part_out, const float* part_lse,
                       int32_t num_parts, int64_t n, int32_t num_heads, int32_t head_dim,
                       int32_t out_dtype, hipStream_t stream) {

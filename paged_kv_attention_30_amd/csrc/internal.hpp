@@ -43,6 +43,28 @@ struct GatherArgs {
   hipStream_t stream;
 };
 
+struct PrologueArgs {
+  void* q_out;             // bf16 [n, Hq, 128], row stride q_out_stride elements
+  int64_t q_out_stride;
+  void* k_cache;           // bf16 pool planes [slots, Hkv, 128], row stride cache_stride
+  void* v_cache;
+  int64_t cache_stride;
+  const void* qkv;         // bf16 [n, (Hq + 2 Hkv) * 128], row stride qkv_stride
+  int64_t qkv_stride;
+  const void* q_norm_w;    // bf16 [128] or null (no q norm)
+  const void* k_norm_w;    // bf16 [128] or null (no k norm)
+  float eps;
+  const int32_t* positions;
+  const float* cache;      // fp32 [max_position, 128]: cos | sin
+  int64_t max_position;
+  const void* out_loc;
+  bool index_is_i64;
+  int64_t n;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  hipStream_t stream;
+};
+
 struct DecodeArgs {
   void* out;               // bf16 [B, Hq, 128]
   float* lse;              // fp32 [B, Hq] or null
@@ -125,6 +147,9 @@ constexpr int kMaxDecodeBlocks = 2048;
 int decode_kv_heads_per_block(int num_kv_heads);
 hipError_t launch_store_kv(const StoreArgs& a);
 hipError_t launch_embedding_gather(const GatherArgs& a);
+hipError_t launch_rope_cache(float* cache, int64_t max_position, int32_t rotary_dim, double base,
+                             hipStream_t stream);
+hipError_t launch_qk_norm_rope_store(const PrologueArgs& a);
 hipError_t launch_paged_decode(const DecodeArgs& a);
 hipError_t launch_paged_extend(const ExtendArgs& a);
 hipError_t launch_merge(const MergeArgs& a);
