@@ -19,8 +19,12 @@
 //   request, several whole requests and the head of another; a request
 //   covered by one workgroup is finished there, a request cut across
 //   workgroups leaves normalised fp32 partials + lse that the merge kernel
-//   combines.  ("Fixed" mode, split_tokens = S > 0: chunk c of request r is
-//   keys [cS, (c+1)S), one workgroup per (chunk, request).)
+//   combines.  One workgroup fills a compute unit: two waves per kv head
+//   take alternate tiles and combine their states in LDS at the end of each
+//   segment (two workgroups per unit were measured slower: the younger one
+//   is served after the older and ends the kernel alone).  ("Fixed" mode,
+//   split_tokens = S > 0: chunk c of request r is keys [cS, (c+1)S), one
+//   workgroup per (chunk, request).)
 // * Keys are processed 32 at a time.  Each lane fetches the page-table entry
 //   of "its" token and issues 16-byte loads of that token's K and V row
 //   segment (a wave reads 64 contiguous bytes per token per instruction).
@@ -47,6 +51,9 @@ namespace {
 
 constexpr int kTile = 32;          // keys per inner iteration
 constexpr int kVtPitch = 32;       // LDS elements per head-dim row of V^T
+// LDS elements of one wave: its V^T tile, then a 128-byte slot for the
+// per-column (max, sum) a paired wave hands over
+constexpr int kWaveLds = kHeadDim * kVtPitch + 64;
 
 struct DecodeParams {
   uint16_t* out;
@@ -115,10 +122,18 @@ __device__ __forceinline__ void write_empty(const DecodeParams& p, int r, int g,
 // One wave: attention of request r's q heads of kv head g over keys
 // [t0, t1) (t0 < t1).  Writes the final bf16 output + lse when `whole`,
 // else the normalised fp32 partial + lse at partial row `slot`.
-// `vt` is the wave's V^T tile (128 x kVtPitch), `qs` its q rows (ratio x 128).
+// `vt` is the wave's V^T tile (128 x kVtPitch), `qs` its group's q rows
+// (ratio x 128).  With NPAR = 2 two waves share the segment: wave `par`
+// takes the tiles t0 + 32 (2i + par); at the end the parity-1 wave leaves
+// its state in its V^T tile (`pvt` is that tile, seen from the pair) and the
+// parity-0 wave folds it in and writes the result.  Every wave of the
+// workgroup must call this for the same segments (it holds workgroup
+// barriers).
+template <int NPAR>
 __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* vt,
-                                               uint16_t* qs, int r, int g, int t0, int t1,
-                                               bool whole, int64_t slot) {
+                                               uint16_t* qs, uint16_t* pvt, int par, int r,
+                                               int g, int t0, int t1, bool whole,
+                                               int64_t slot) {
   const int lane = __lane_id();
   const int c = lane & 15;      // q-head column / token row inside the MFMA
   const int j = lane >> 4;      // k-slot group
@@ -156,8 +171,10 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
 
   // The page-table entries of tile i+1 are fetched while tile i computes,
   // so each iteration waits on one memory latency (its K/V), not two.
-  int na = pt[min(t0 + c, t1 - 1)];
-  int nb = pt[min(t0 + 16 + c, t1 - 1)];
+  constexpr int kStep = kTile * NPAR;
+  const int tfirst = t0 + kTile * par;
+  int na = pt[min(tfirst + c, t1 - 1)];
+  int nb = pt[min(tfirst + 16 + c, t1 - 1)];
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -166,7 +183,7 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
   }
   __builtin_amdgcn_wave_barrier();
 
-  for (int tb = t0; tb < t1; tb += kTile) {
+  for (int tb = tfirst; tb < t1; tb += kStep) {
     const char* ra = kbase + (int64_t)na * cs;
     const char* rb = kbase + (int64_t)nb * cs;
     // V first: it goes to LDS as soon as it lands, which frees its
@@ -182,9 +199,9 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
       ka[kk] = ld16(ra + 64 * kk);
       kb[kk] = ld16(rb + 64 * kk);
     }
-    if (tb + kTile < t1) {
-      na = pt[min(tb + kTile + c, t1 - 1)];
-      nb = pt[min(tb + kTile + 16 + c, t1 - 1)];
+    if (tb + kStep < t1) {
+      na = pt[min(tb + kStep + c, t1 - 1)];
+      nb = pt[min(tb + kStep + 16 + c, t1 - 1)];
     }
 
     // V^T tile: lane holds V[key c][dims 32kk+8j .. +7] and V[key 16+c][...]
@@ -253,6 +270,35 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
 
   float l_tot = l_run + shfl_xor(l_run, 16);
   l_tot += shfl_xor(l_tot, 32);
+  if (NPAR > 1) {
+    // the parity-1 wave's state: acc as [mb][lane] f32x4 in its V^T tile,
+    // (max, sum) per head column in the slot after it
+    f32x4* xacc = reinterpret_cast<f32x4*>(pvt);
+    float* xml = reinterpret_cast<float*>(pvt + kHeadDim * kVtPitch);
+    if (par == 1) {
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) xacc[mb * 64 + lane] = acc[mb];
+      if (j == 0) {
+        xml[c] = m_run;
+        xml[16 + c] = l_tot;
+      }
+    }
+    __syncthreads();
+    if (par == 0) {
+      // fold in the partner's keys (it may have had no tile: max -inf)
+      const float m1 = xml[c];
+      const float l1 = xml[16 + c];
+      const float mm = fmaxf(m_run, m1);
+      const float a0 = fast_exp2(m_run - mm);
+      const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) acc[mb] = acc[mb] * a0 + xacc[mb * 64 + lane] * a1;
+      l_tot = l_tot * a0 + l1 * a1;
+      m_run = mm;
+    }
+    __syncthreads();
+    if (par != 0) return;
+  }
   if (c >= R) return;
   const int h = g * R + c;
   const float inv = 1.f / l_tot;
@@ -280,9 +326,14 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
   }
 }
 
-// LDS of one wave: its V^T tile, then its q rows.
-__device__ __forceinline__ uint16_t* wave_lds(uint16_t* base, int w, int ratio) {
-  return base + (size_t)w * (kHeadDim * kVtPitch + ratio * kHeadDim);
+// LDS of a workgroup with `nw` waves: the V^T tile (+ hand-over slot) of
+// every wave, then the q rows of every kv-head group (shared by the waves of
+// a pair).
+__device__ __forceinline__ uint16_t* wave_vt(uint16_t* base, int w) {
+  return base + (size_t)w * kWaveLds;
+}
+__device__ __forceinline__ uint16_t* group_qs(uint16_t* base, int nw, int gi, int ratio) {
+  return base + (size_t)nw * kWaveLds + (size_t)gi * ratio * kHeadDim;
 }
 
 // Fixed chunks: workgroup (chunk, request) = blockIdx.x.
@@ -292,8 +343,8 @@ decode_fixed_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t dyn_lds[];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  uint16_t* vt = wave_lds(dyn_lds, w, p.ratio);
-  uint16_t* qs = vt + kHeadDim * kVtPitch;
+  uint16_t* vt = wave_vt(dyn_lds, w);
+  uint16_t* qs = group_qs(dyn_lds, KVB, w, p.ratio);
   const int r = blockIdx.x % p.batch;
   const int split = blockIdx.x / p.batch;
   const int g = blockIdx.y * KVB + w;
@@ -309,19 +360,23 @@ decode_fixed_kernel(DecodeParams p) {
   // no chunk index ever exceeds the workspace
   const int nsplit = min((L + S - 1) / S, p.max_splits);
   const int t1 = (split == p.max_splits - 1) ? L : min(t0 + S, L);
-  attend_segment(p, vt, qs, r, g, t0, t1, nsplit == 1, (int64_t)split * p.batch + r);
+  attend_segment<1>(p, vt, qs, vt, 0, r, g, t0, t1, nsplit == 1, (int64_t)split * p.batch + r);
 }
 
 // Balanced ranges: workgroup b of G owns flattened keys [b*T/G, (b+1)*T/G).
-template <int KVB>
-__global__ void __launch_bounds__(KVB * 64, 4)
+// NPAR = 2: two waves per kv head (one workgroup fills a compute unit).
+template <int KVB, int NPAR>
+__global__ void __launch_bounds__(KVB * 64 * NPAR, 4)
 decode_balanced_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t dyn_lds[];
   const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
-  uint16_t* vt = wave_lds(dyn_lds, w, p.ratio);
-  uint16_t* qs = vt + kHeadDim * kVtPitch;
-  const int g = blockIdx.y * KVB + w;
+  const int wk = w % KVB;
+  const int par = w / KVB;
+  uint16_t* vt = wave_vt(dyn_lds, w);
+  uint16_t* pvt = wave_vt(dyn_lds, wk + KVB * (NPAR - 1));
+  uint16_t* qs = group_qs(dyn_lds, KVB * NPAR, wk, p.ratio);
+  const int g = blockIdx.y * KVB + wk;
   const int b = blockIdx.x;
   const int Ggrid = gridDim.x;
   const int B = p.batch;
@@ -379,7 +434,7 @@ decode_balanced_kernel(DecodeParams p) {
     if (r < 0) break;
     r_prev = r;
     if (r1 == r0) {
-      write_empty(p, r, g, lane & 15, lane >> 4);
+      if (par == 0) write_empty(p, r, g, lane & 15, lane >> 4);
       if (writer) {
         p.meta[2 * r] = -1;
         p.meta[2 * r + 1] = -1;
@@ -389,7 +444,7 @@ decode_balanced_kernel(DecodeParams p) {
     const int s0 = (int)(max(start, r0) - r0);
     const int s1 = (int)(min(end, r1) - r0);
     const bool whole = r0 >= start && r1 <= end;
-    attend_segment(p, vt, qs, r, g, s0, s1, whole, (int64_t)b + r);
+    attend_segment<NPAR>(p, vt, qs, pvt, par, r, g, s0, s1, whole, (int64_t)b + r);
     if (writer) {
       // workgroups holding the first and the last key of request r
       const int64_t bf = ((r0 + 1) * G - 1) / T;
@@ -400,13 +455,16 @@ decode_balanced_kernel(DecodeParams p) {
   }
 }
 
-size_t decode_lds_bytes(int kvb, int ratio) {
-  return (size_t)kvb * (kHeadDim * kVtPitch + ratio * kHeadDim) * sizeof(uint16_t);
+size_t decode_lds_bytes(int kvb, int npar, int ratio) {
+  return ((size_t)kvb * npar * kWaveLds + (size_t)kvb * ratio * kHeadDim) * sizeof(uint16_t);
 }
+
+// LDS a workgroup may hold on gfx950
+constexpr size_t kLdsLimit = 160 * 1024;
 
 // Workgroups of the balanced kernel resident per compute unit (cached per
 // device and ratio).
-template <int KVB>
+template <int KVB, int NPAR>
 int resident_blocks_per_cu(int ratio) {
   static int cached[64][5] = {};
   int dev = 0;
@@ -414,24 +472,34 @@ int resident_blocks_per_cu(int ratio) {
   const int ri = ratio == 1 ? 0 : ratio == 2 ? 1 : ratio == 4 ? 2 : ratio == 8 ? 3 : 4;
   if (cached[dev][ri] > 0) return cached[dev][ri];
   int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_balanced_kernel<KVB>, KVB * 64,
-                                                   decode_lds_bytes(KVB, ratio)) != hipSuccess ||
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_balanced_kernel<KVB, NPAR>,
+                                                   KVB * 64 * NPAR,
+                                                   decode_lds_bytes(KVB, NPAR, ratio)) != hipSuccess ||
       n <= 0)
     n = 1;
   cached[dev][ri] = n;
   return n;
 }
 
+template <int KVB, int NPAR>
+hipError_t launch_balanced(const DecodeArgs& a, const DecodeParams& p) {
+  const unsigned gy = (unsigned)(a.num_kv_heads / KVB);
+  int64_t g = (int64_t)a.balanced_blocks * resident_blocks_per_cu<KVB, NPAR>(p.ratio) / gy;
+  if (g < 1) g = 1;
+  if (g > kMaxDecodeBlocks) g = kMaxDecodeBlocks;
+  hipLaunchKernelGGL((decode_balanced_kernel<KVB, NPAR>), dim3((unsigned)g, gy),
+                     dim3(KVB * 64 * NPAR), decode_lds_bytes(KVB, NPAR, p.ratio), a.stream, p);
+  return hipGetLastError();
+}
+
 template <int KVB>
 hipError_t launch_kvb(const DecodeArgs& a, const DecodeParams& p) {
   const unsigned gy = (unsigned)(a.num_kv_heads / KVB);
-  const size_t lds = decode_lds_bytes(KVB, p.ratio);
+  const size_t lds = decode_lds_bytes(KVB, 1, p.ratio);
   if (a.balanced_blocks > 0) {
-    int64_t g = (int64_t)a.balanced_blocks * resident_blocks_per_cu<KVB>(p.ratio) / gy;
-    if (g < 1) g = 1;
-    if (g > kMaxDecodeBlocks) g = kMaxDecodeBlocks;
-    hipLaunchKernelGGL((decode_balanced_kernel<KVB>), dim3((unsigned)g, gy), dim3(KVB * 64), lds,
-                       a.stream, p);
+    // two waves per kv head when their LDS fits
+    if (decode_lds_bytes(KVB, 2, p.ratio) <= kLdsLimit) return launch_balanced<KVB, 2>(a, p);
+    return launch_balanced<KVB, 1>(a, p);
   } else {
     dim3 grid((unsigned)((int64_t)a.max_splits * a.batch), gy);
     hipLaunchKernelGGL((decode_fixed_kernel<KVB>), grid, dim3(KVB * 64), lds, a.stream, p);

@@ -257,6 +257,36 @@ def test_decode_balanced_ranges_edge_cases(lens_kind):
     assert_lse_close(lse[torch.from_numpy(sample).cuda()], rl, f"balanced {lens_kind}")
 
 
+def test_decode_workspace_reused_across_shapes():
+    """One workspace serves calls of different shapes in a row (its contents on
+    entry are ignored)."""
+    banner("decode workspace reuse")
+    cases = [(32, 8, np.random.default_rng(3).integers(1, 2000, 60)),
+             (16, 8, [64, 65, 255, 256, 257, 600]),
+             (64, 8, [1500, 2048, 3, 777]),
+             (8, 2, [900, 1, 400]),
+             (32, 8, np.random.default_rng(4).integers(500, 3000, 20))]
+    need = max(msgl.paged_decode_workspace_size(len(lens), hq, hkv, int(np.max(lens)))[0]
+               for hq, hkv, lens in cases)
+    ws = msgl.alloc_workspace(need)
+    ws.fill_(0x7f)
+    for k in range(2 * len(cases)):
+        hq, hkv, lens = cases[k % len(cases)]
+        inp = small_decode(80 + k % len(cases), hq, hkv, np.asarray(lens), num_slots=1 << 17)
+        u = Uploaded(inp)
+        u.store()
+        out, lse = msgl.paged_decode(u.dq, u.k, u.v, u.pt, u.d_lens, u.d_max, inp.sm_scale,
+                                     req_rows=u.d_rows, workspace=ws)
+        torch.cuda.synchronize()
+        kp, vp = oracle_pool(inp)
+        sel = np.unique(np.linspace(0, len(inp.dec_seq_lens) - 1, 12).astype(int))
+        ro, rl = oracle.paged_decode(inp.dec_q[sel], kp, vp, inp.page_table, inp.dec_req_rows[sel],
+                                     inp.dec_seq_lens[sel], inp.sm_scale, inp.num_kv_heads)
+        t = torch.from_numpy(sel).cuda()
+        assert_close(out[t], ro, f"reuse call {k}")
+        assert_lse_close(lse[t], rl, f"reuse call {k}")
+
+
 def test_decode_zero_scale_is_mean_of_values():
     banner("decode sm_scale=0")
     inp = small_decode(66, 32, 8, [100, 37], num_slots=1024, sm_scale=0.0)
