@@ -44,6 +44,7 @@ namespace msgl {
 namespace {
 
 constexpr int kBN = 64;            // keys per tile
+constexpr int kPvDepth = 3;        // V^T operand reads in flight ahead of the P V MFMAs
 constexpr int kTileElems = kBN * kHeadDim;   // one K or V tile, bf16 elements
 constexpr int kPieces = kTileElems * 2 / 1024;  // 1-KiB LDS pieces per K (or V) tile
 
@@ -353,16 +354,26 @@ paged_extend_kernel(ExtendParams p) {
     __builtin_amdgcn_s_setprio(1);
 
     // O^T += V^T P^T: slot (jh, e) of step u is key 16u + 8(e/4) + 4jh + e%4
+    // 16 steps (u, mb) with the accumulator changing every step; the
+    // operands of step st + kPvDepth - 1 are read while step st's MFMA runs
+    // (the fences keep that order, so an LDS read is never waited for right
+    // after it is issued)
+    auto rdv = [&](int st) __attribute__((always_inline)) {
+      const int u = st >> 2, mb = st & 3;
+      const int key_lo = 16 * u + 4 * jh + tr_key;
+      const u32x2 lo = lds_read_tr16(vt_lds + v_off(key_lo, 8 * mb + tr_cg));
+      const u32x2 hi = lds_read_tr16(vt_lds + v_off(key_lo + 8, 8 * mb + tr_cg));
+      return u32x4{lo[0], lo[1], hi[0], hi[1]};
+    };
+    u32x4 va[kPvDepth];
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb) {
+    for (int d = 0; d < kPvDepth - 1; ++d) va[d] = rdv(d);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int key_lo = 16 * u + 4 * jh + tr_key;
-        const u32x2 lo = lds_read_tr16(vt_lds + v_off(key_lo, 8 * mb + tr_cg));
-        const u32x2 hi = lds_read_tr16(vt_lds + v_off(key_lo + 8, 8 * mb + tr_cg));
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-        acc[mb] = mfma32x32x16(a, pb[u], acc[mb]);
-      }
+    for (int st = 0; st < 16; ++st) {
+      if (st + kPvDepth - 1 < 16) va[(st + kPvDepth - 1) % kPvDepth] = rdv(st + kPvDepth - 1);
+      __builtin_amdgcn_sched_barrier(0);
+      acc[st & 3] = mfma32x32x16(va[st % kPvDepth], pb[st >> 2], acc[st & 3]);
+      __builtin_amdgcn_sched_barrier(0);
     }
     __builtin_amdgcn_s_setprio(0);
   };
