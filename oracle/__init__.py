@@ -11,8 +11,12 @@ Everything here is written from the definitions on the source pages
 upcast.  See ``oracle/attention.py``, ``oracle/embedding.py`` and
 ``oracle/prologue.py`` for the
 functions and their pins (the ``tests/test_oracle_*.py`` files); every
-function is pinned.
+function is pinned.  ``oracle/radix.py`` is the integer host logic of the
+KV cache manager (page allocator + radix prefix cache), pinned in
+``tests/test_oracle_radix.py``.
 """
+
+from .radix import KVCacheOracle, compare_key  # noqa: F401
 
 from .embedding import embedding_gather  # noqa: F401
 from .prologue import rope_cache, rms_norm, rope, qk_norm_rope_store  # noqa: F401
