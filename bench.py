@@ -51,6 +51,9 @@ WORKLOAD_TEXT = {
            "positions 0..8191, Hq 32 / Hkv 8 / D 128 (Qwen3-8B-class), merged qkv bf16 N(0,1), "
            "norm weights N(0,1), RoPE base 1e6, slots a random permutation of a 524,288-slot pool, "
            "seed 42",
+    "KVC": "host KV cache manager (page allocator + radix prefix cache, C++): 1,024 requests, "
+           "each one of 32 Zipf(1.1)-popular 1,024-token system prompts + 128..256 own tokens, "
+           "32..64 decode steps, page_size 16, 262,144-slot pool, 128 rows, seed 7",
     "EMB": "embedding gather: 8,192 token ids uniform over a 151,936 x 4,096 bf16 table "
            "(Qwen3-8B-class vocabulary and hidden size, one tensor-parallel rank), ids int32, "
            "table N(0,1), seed 41",
@@ -369,6 +372,64 @@ def prologue_run(steps: int, warmup: int):
             "tokens_per_s": round(T / (ms * 1e-3), 1)}
 
 
+def kvcache_run():
+    """Host-only: a request trace through the C++ manager (via the binding, with
+    the Python scheduling loop of workloads.kvtrace.drive) and, on a sample,
+    through the oracle; plus per-call match / key-compare times."""
+    import time
+    from workloads.kvtrace import kv_trace, drive
+    import oracle
+    import paged_kv_attention_30_amd as msgl
+    tr = kv_trace()
+    kv = msgl.KVCache(tr.num_slots, tr.page_size, tr.max_rows, tr.max_len)
+    t0 = time.perf_counter()
+    st = drive(kv, tr)
+    t_cpp = time.perf_counter() - t0
+    sample = kv_trace(num_requests=128)
+    ko = oracle.KVCacheOracle(sample.num_slots, sample.page_size, sample.max_rows, sample.max_len)
+    t0 = time.perf_counter()
+    drive(ko, sample)
+    t_or = time.perf_counter() - t0
+    # per call: match of a cached 1,280-token prompt (warm tree), key compare of
+    # two equal 1,024-token runs
+    ids = tr.prompts[0]
+    kv.match(ids)
+    ko2 = oracle.KVCacheOracle(tr.num_slots, tr.page_size, tr.max_rows, tr.max_len)
+    drive(ko2, kv_trace(num_requests=8))
+    ids8 = kv_trace(num_requests=8).prompts[0]
+    reps = 2000
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        kv.match(ids8)
+    m_cpp = (time.perf_counter() - t0) / reps
+    t0 = time.perf_counter()
+    for _ in range(200):
+        ko2.match(ids8)
+    m_or = (time.perf_counter() - t0) / 200
+    a = np.arange(1024, dtype=np.int32)
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        msgl.compare_key(a, a)
+    c_cpp = (time.perf_counter() - t0) / reps
+    t0 = time.perf_counter()
+    for _ in range(200):
+        oracle.compare_key(a, a)
+    c_or = (time.perf_counter() - t0) / 200
+    kv.close()
+    return {"workload": WORKLOAD_TEXT["KVC"], "requests": st["admitted"],
+            "prefix_reuse": round(st["matched_tokens"] / st["prompt_tokens"], 4),
+            "decode_tokens": st["decode_tokens"], "manager_calls": st["calls"],
+            "trace_s": round(t_cpp, 4), "requests_per_s": round(st["admitted"] / t_cpp, 1),
+            "calls_per_s": round(st["calls"] / t_cpp, 1),
+            "match_us": round(m_cpp * 1e6, 2), "compare_key_1024_us": round(c_cpp * 1e6, 3),
+            "note": "times include the Python scheduling loop and ctypes marshalling",
+            "cpu_baseline": {"kind": "oracle", "cores": 1,
+                             "requests_per_s": round(128 / t_or, 1),
+                             "match_us": round(m_or * 1e6, 2),
+                             "compare_key_1024_us": round(c_or * 1e6, 3),
+                             "sample": "first 128 requests of the same trace"}}
+
+
 def decode_figures(inp, res, steps):
     from workloads import metrics
     kv = metrics.decode_kv_bytes(inp.page_table, inp.dec_req_rows, inp.dec_seq_lens,
@@ -438,6 +499,9 @@ def main(argv=None) -> int:
     from workloads import make_config
 
     msgl.load()
+    if args.only == "KVC":
+        print(json.dumps({"only": "KVC", **kvcache_run()}))
+        return 0
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
@@ -482,7 +546,7 @@ def main(argv=None) -> int:
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": "decode_balanced_kernel<8> + merge_kernel (one msgl_paged_decode call)",
+                "kernel": "decode_balanced_kernel<8, 2> + merge_kernel (one msgl_paged_decode call)",
                 "alg_bytes_per_launch": alg, "avg_launch_ms": round(dec_ms, 4)}
     del run
     torch.cuda.empty_cache()

@@ -26,3 +26,4 @@ from .binding import (  # noqa: F401
     alloc_workspace,
 )
 from ._build import LIB_PATH  # noqa: F401
+from .kvcache import KVCache, compare_key  # noqa: F401

@@ -1,7 +1,8 @@
 """Build the HIP library (libmsgl.so) for gfx950 with hipcc, in-tree.
 
-Compiles every ``csrc/*.hip`` translation unit in parallel into
-``_build/`` and links them into ``paged_kv_attention_30_amd/libmsgl.so``.
+Compiles every ``csrc/*.hip`` translation unit (hipcc) and every host-only
+``csrc/*.cpp`` one (g++) in parallel into ``_build/`` and links them into
+``paged_kv_attention_30_amd/libmsgl.so``.
 Always recompiles (the caller asked for a build).
 """
 
@@ -41,8 +42,18 @@ def hipcc() -> str:
     return path
 
 
+HOST_FLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-I", os.path.join(ROOT, "include")]
+
+
 def sources() -> list[str]:
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
+
+
+def host_cxx() -> str:
+    path = shutil.which("g++")
+    if not path:
+        raise RuntimeError("g++ not found: the host compiler is required to build libmsgl")
+    return path
 
 
 def _run(cmd: list[str]) -> None:
@@ -62,9 +73,13 @@ def build(verbose: bool = False) -> str:
     objs = []
     cmds = []
     for src in sources():
-        obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
+        stem, ext = os.path.splitext(os.path.basename(src))
+        obj = os.path.join(BUILD, stem + ".o")
         objs.append(obj)
-        cmds.append([cc, *COMMON_FLAGS, "-c", src, "-o", obj])
+        if ext == ".cpp":
+            cmds.append([host_cxx(), *HOST_FLAGS, "-c", src, "-o", obj])
+        else:
+            cmds.append([cc, *COMMON_FLAGS, "-c", src, "-o", obj])
     with ThreadPoolExecutor(min(8, len(cmds))) as ex:
         list(ex.map(_run, cmds))
     tmp = LIB_PATH + ".tmp"

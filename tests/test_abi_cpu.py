@@ -40,6 +40,16 @@ def test_every_declared_symbol_is_exported(lib):
         assert name in binding.SIGNATURES, f"{name} has no ctypes signature"
 
 
+def test_every_kvcache_symbol_is_exported(lib):
+    from paged_kv_attention_30_amd import kvcache
+    text = open(os.path.join(ROOT, "include", "msgl_kvcache.h")).read()
+    names = sorted(set(re.findall(r"^\s*(?:[\w\s\*]+?)\b(msgl_\w+)\s*\(", text, re.M)))
+    assert len(names) >= 15
+    for name in names:
+        assert hasattr(lib, name), f"{name} declared in msgl_kvcache.h but not exported"
+        assert name in kvcache._SIGS, f"{name} has no ctypes signature"
+
+
 def test_status_strings_and_version(lib):
     assert lib.msgl_version() >= 100
     for code in (OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH):

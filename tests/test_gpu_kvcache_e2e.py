@@ -1,0 +1,100 @@
+"""The page tables the host KV cache manager produces drive the attention
+kernels: store_kv at the slots it allocates, extend over a prefix it matched
+(shared pages of another request), decode steps on the rows it grows — each
+checked against the fp64 oracle on the same table, and page_size 16 against
+page_size 1 bit for bit.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_attention_30_amd as msgl
+from workloads import random_bf16
+from tests.gpu_util import up, bits, assert_close, assert_lse_close
+
+pytestmark = pytest.mark.gpu
+
+P, S, HQ, HKV, D = 16, 8192, 32, 8, 128
+SCALE = 1.0 / np.sqrt(D)
+
+
+def banner(msg):
+    print(f"[gpu-kvc] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def test_manager_page_tables_drive_store_extend_and_decode():
+    rng = np.random.default_rng(21)
+    kv = msgl.KVCache(S, P, 8, 1024)
+    kp = random_bf16(rng, (S, HKV, D))
+    vp = random_bf16(rng, (S, HKV, D))
+    k_dev, v_dev = up(kp), up(vp)
+    system = list(rng.integers(0, 1000, 256))
+    prompts = {"A": system + list(rng.integers(0, 1000, 60)),
+               "B": system + list(rng.integers(0, 1000, 90)),
+               "C": list(rng.integers(1000, 2000, 130))}
+    running = {}
+    for name, ids in prompts.items():
+        banner(f"prefill {name}")
+        st, row = kv.alloc_row()
+        st, cached, h = kv.match(ids, row)
+        assert st == 0 and kv.lock(h, 1) == 0
+        if name == "B":
+            assert cached == 256                       # A's system prompt, page aligned
+            assert np.array_equal(kv.page_table[row, :256], kv.page_table[running["A"][0], :256])
+        assert kv.allocate([row], [cached], [len(ids)]) == 0
+        E = len(ids) - cached
+        loc = kv.page_table[row, cached:len(ids)].astype(np.int64)
+        k_new, v_new = random_bf16(rng, (E, HKV, D)), random_bf16(rng, (E, HKV, D))
+        msgl.store_kv(k_dev, v_dev, up(k_new), up(v_new), up(loc))
+        kp, vp = oracle.store_kv(kp, vp, k_new, v_new, loc)
+        q = random_bf16(rng, (E, HQ, D))
+        table = kv.page_table.copy()
+        args = (up(q), k_dev, v_dev, up(table), up(np.array([cached], np.int32)),
+                up(np.array([E], np.int32)), up(np.array([0, E], np.int32)), E, len(ids), SCALE)
+        o16, l16 = msgl.paged_extend(*args, req_rows=up(np.array([row], np.int32)), page_size=P)
+        o1, _ = msgl.paged_extend(*args, req_rows=up(np.array([row], np.int32)), page_size=1)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o16), bits(o1))
+        ro, rl = oracle.paged_extend(q, kp, vp, table, np.array([row]), np.array([cached]),
+                                     np.array([E]), np.array([0, E]), SCALE, HKV)
+        assert_close(o16, ro, f"extend {name}")
+        assert_lse_close(l16, rl, f"extend {name}")
+        st, h2, n2 = kv.cache_req(row, ids, len(ids), h, False)
+        assert st == 0 and n2 == len(ids) - len(ids) % P
+        running[name] = [row, list(ids), len(ids), h2]
+    for step in range(20):
+        rows = [running[n][0] for n in running]
+        lens = [running[n][2] for n in running]
+        assert kv.allocate(rows, lens, [x + 1 for x in lens]) == 0
+        loc = np.array([kv.page_table[r, n] for r, n in zip(rows, lens)], np.int64)
+        k_new, v_new = random_bf16(rng, (len(rows), HKV, D)), random_bf16(rng, (len(rows), HKV, D))
+        msgl.store_kv(k_dev, v_dev, up(k_new), up(v_new), up(loc))
+        kp, vp = oracle.store_kv(kp, vp, k_new, v_new, loc)
+        for n in running:
+            running[n][1].append(int(rng.integers(0, 1000)))
+            running[n][2] += 1
+        seq = np.array([x + 1 for x in lens], np.int32)
+        q = random_bf16(rng, (len(rows), HQ, D))
+        table = kv.page_table.copy()
+        o16, l16 = msgl.paged_decode(up(q), k_dev, v_dev, up(table), up(seq), int(seq.max()), SCALE,
+                                     req_rows=up(np.array(rows, np.int32)), page_size=P)
+        o1, _ = msgl.paged_decode(up(q), k_dev, v_dev, up(table), up(seq), int(seq.max()), SCALE,
+                                  req_rows=up(np.array(rows, np.int32)), page_size=1)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(o16), bits(o1))
+        if step % 5 == 4:
+            banner(f"decode step {step}")
+            ro, rl = oracle.paged_decode(q, kp, vp, table, np.array(rows), seq, SCALE, HKV)
+            assert_close(o16, ro, f"decode step {step}")
+            assert_lse_close(l16, rl, f"decode step {step}")
+    for name, (row, ids, n, h) in running.items():
+        st, _, _ = kv.cache_req(row, ids, n, h, True)
+        assert st == 0 and kv.free_row(row) == 0
+    # three requests cached: the tree holds what they computed, the rest is free
+    free_pages, evictable, protected = kv.stats()[:3]
+    assert protected == 0 and free_pages * P + evictable == S
