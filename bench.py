@@ -237,7 +237,7 @@ def cold_decode_ms(run: Run, reps: int = 10):
     graphs = getattr(run, "graphs", None)
     call = graphs["decode"].replay if graphs else run.decode
     for _ in range(reps):
-        torch.sum(scratch, out=sink)
+        torch.sum(scratch, dim=0, out=sink)
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
         a.record()
