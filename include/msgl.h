@@ -282,6 +282,59 @@ int msgl_merge_states(void* out, float* lse_out, const float* part_out,
                       int32_t num_heads, int32_t head_dim, int32_t out_dtype,
                       hipStream_t stream);
 
+/*
+ * Graph-replayed decode step ["Mini-SGLang complete analysis" §4.6.6 (the
+ * attention backend's persistent capture buffers, live data written in place
+ * before replay), §5.3 (one graph per batch size of [1, 2, 4, 8, 16, 24, ...,
+ * max_bs], padding to the next size with a dummy request on a sentinel page)].
+ *
+ * A msgl_decode_graph owns one captured HIP graph per ladder size, each
+ * holding store_kv + paged_decode (balanced split-KV) for that many rows of
+ * fixed-address buffers carved from caller memory `buffer`:
+ *   q      bf16 [max_bs, num_q_heads, 128]     k_new, v_new  bf16 [max_bs, num_kv_heads, 128]
+ *   out    bf16 [max_bs, num_q_heads, 128]     lse           fp32 [max_bs, num_q_heads]
+ *   seq_lens, req_rows, out_loc  int32 [max_bs]   then the decode workspace,
+ * at the byte offsets msgl_decode_graph_layout() gives (offsets[0..8] in
+ * that order, offsets[9] = bytes needed; every region 256-byte aligned).
+ * Per step the caller writes rows [0, batch) of q, k_new, v_new, seq_lens
+ * (counting the new token), req_rows and out_loc, then calls
+ * msgl_decode_graph_run(batch): rows [batch, bucket) are turned into the
+ * dummy request (seq_len 1, page-table row dummy_row, out_loc
+ * sentinel_slot, zero q/k/v) and the bucket's graph is replayed on `stream`.
+ * Results: rows [0, batch) of out / lse.
+ *
+ *   page_table[dummy_row, 0] must hold sentinel_slot, a slot no request owns
+ *   (the pages reserve one extra page for it); padded rows all write zeros
+ *   there, and so does create (its warm-up runs fully padded batches).  The pool, the page table and the buffer must stay at their
+ *   addresses while the graph lives.
+ * create: validates (same rules as the two calls), warms up and captures on a
+ *   private stream, synchronises it; allocates the graphs (host/runtime
+ *   objects) — a set-up call.  run: two launches (padding + graph), no
+ *   allocation, no synchronisation.  Replays on one graph must not overlap
+ *   (they share the buffers).  The padding, the graph and the results follow
+ *   the stream order of `stream`.
+ */
+typedef struct msgl_decode_graph msgl_decode_graph;
+
+int msgl_decode_graph_layout(int32_t max_bs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t max_seq_len, size_t* offsets /* [10] */);
+
+int msgl_decode_graph_create(void* k_cache, void* v_cache, int64_t num_slots,
+                             int64_t cache_row_stride, const int32_t* page_table,
+                             int64_t page_table_stride, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t page_size, int32_t max_bs,
+                             int32_t max_seq_len, float sm_scale, int32_t dummy_row,
+                             int32_t sentinel_slot, void* buffer, size_t buffer_bytes,
+                             msgl_decode_graph** out);
+
+/* batch in [0, max_bs]; 0 enqueues nothing. */
+int msgl_decode_graph_run(msgl_decode_graph* graph, int32_t batch, hipStream_t stream);
+
+/* Captured size a batch replays (-1 if out of range). */
+int32_t msgl_decode_graph_bucket(const msgl_decode_graph* graph, int32_t batch);
+
+void msgl_decode_graph_destroy(msgl_decode_graph* graph);
+
 #ifdef __cplusplus
 }
 #endif

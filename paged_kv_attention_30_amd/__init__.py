@@ -24,6 +24,7 @@ from .binding import (  # noqa: F401
     plan_qk_norm_rope_store,
     plan_embedding_gather,
     alloc_workspace,
+    DecodeGraph,
 )
 from ._build import LIB_PATH  # noqa: F401
 from .kvcache import KVCache, compare_key  # noqa: F401

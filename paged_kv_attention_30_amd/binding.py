@@ -56,6 +56,13 @@ SIGNATURES = {
                                        _c_void_p, _i64, _c_void_p, _c_void_p, _f32, _c_void_p,
                                        _c_void_p, _i64, _c_void_p, _i32, _i64, _i32, _i32, _i32,
                                        _c_void_p]),
+    "msgl_decode_graph_layout": (_i32, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_size_t)]),
+    "msgl_decode_graph_create": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _i64, _i32,
+                                        _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+                                        _c_void_p, _size_t, ctypes.POINTER(_c_void_p)]),
+    "msgl_decode_graph_run": (_i32, [_c_void_p, _i32, _c_void_p]),
+    "msgl_decode_graph_bucket": (_i32, [_c_void_p, _i32]),
+    "msgl_decode_graph_destroy": (None, [_c_void_p]),
 }
 
 
@@ -484,3 +491,68 @@ def qk_norm_rope_store(qkv, k_cache, v_cache, positions, cos_sin_cache, out_loc,
     return plan_qk_norm_rope_store(qkv, k_cache, v_cache, positions, cos_sin_cache, out_loc,
                                    num_q_heads, num_kv_heads, q_norm_weight, k_norm_weight, eps,
                                    q_out).run(stream)
+
+
+class DecodeGraph:
+    """Graph-replayed decode step (``msgl_decode_graph_*``): store_kv +
+    paged_decode captured per batch size of the ladder [1, 2, 4, 8, 16, ...,
+    max_bs] over fixed buffers.  Write rows [0, batch) of ``q``, ``k_new``,
+    ``v_new``, ``seq_lens``, ``req_rows``, ``out_loc`` (torch views of the
+    buffer), call ``run(batch)``, read rows [0, batch) of ``out`` / ``lse``.
+    ``page_table[dummy_row, 0]`` must be ``sentinel_slot``, a slot no request
+    owns."""
+
+    def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: torch.Tensor,
+                 num_q_heads: int, max_bs: int, max_seq_len: int, sm_scale: float,
+                 dummy_row: int, sentinel_slot: int, page_size: int = 1):
+        lib = load()
+        _need(k_cache, torch.bfloat16, "k_cache", 3)
+        _need(page_table, torch.int32, "page_table", 2)
+        slots, hkv, d = k_cache.shape
+        off = (_size_t * 10)()
+        _check(lib.msgl_decode_graph_layout(max_bs, num_q_heads, hkv, d, max_seq_len, off),
+               "msgl_decode_graph_layout")
+        self.buffer = torch.zeros(int(off[9]), dtype=torch.uint8, device=k_cache.device)
+        self._keep = (k_cache, v_cache, page_table)
+
+        def view(i, dtype, shape):
+            n = 1
+            for x in shape:
+                n *= x
+            nbytes = n * torch.empty((), dtype=dtype).element_size()
+            return self.buffer[off[i]:off[i] + nbytes].view(dtype).view(*shape)
+
+        self.q = view(0, torch.bfloat16, (max_bs, num_q_heads, d))
+        self.k_new = view(1, torch.bfloat16, (max_bs, hkv, d))
+        self.v_new = view(2, torch.bfloat16, (max_bs, hkv, d))
+        self.out = view(3, torch.bfloat16, (max_bs, num_q_heads, d))
+        self.lse = view(4, torch.float32, (max_bs, num_q_heads))
+        self.seq_lens = view(5, torch.int32, (max_bs,))
+        self.req_rows = view(6, torch.int32, (max_bs,))
+        self.out_loc = view(7, torch.int32, (max_bs,))
+        h = _c_void_p()
+        _check(lib.msgl_decode_graph_create(
+            k_cache.data_ptr(), v_cache.data_ptr(), slots, k_cache.stride(0),
+            page_table.data_ptr(), page_table.stride(0), num_q_heads, hkv, d, page_size, max_bs,
+            max_seq_len, sm_scale, dummy_row, sentinel_slot, self.buffer.data_ptr(),
+            self.buffer.numel(), ctypes.byref(h)), "msgl_decode_graph_create")
+        self._h = h
+        self.max_bs = max_bs
+
+    def bucket(self, batch: int) -> int:
+        return int(load().msgl_decode_graph_bucket(self._h, batch))
+
+    def run(self, batch: int, stream=None):
+        _check(load().msgl_decode_graph_run(self._h, batch, _stream(stream)), "msgl_decode_graph_run")
+        return self.out[:batch], self.lse[:batch]
+
+    def close(self):
+        if getattr(self, "_h", None):
+            load().msgl_decode_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

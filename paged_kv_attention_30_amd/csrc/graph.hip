@@ -1,0 +1,248 @@
+// Graph-replayed decode step: store_kv + paged_decode captured once per batch
+// size of a ladder, replayed on fixed-address buffers.
+//
+// "Mini-SGLang complete analysis" §4.6.6 (CUDA graphs and attention): the
+// backend keeps persistent device buffers (seq_lens, positions, cu_seqlens,
+// page table) that every captured batch points at; at run time the live data
+// are written into them in place and the graph for the batch size is
+// replayed.  §5.3: one graph per size of [1, 2, 4, 8, 16, 24, ..., max_bs],
+// captured from the largest down; batches are padded up to the next captured
+// size with a dummy request whose page points at one extra sentinel page, so
+// any padding is safe.  §4.6.5: for decode the per-request query count is 1,
+// so the query offsets are a constant arange (here: implicit in the decode
+// call's layout).
+//
+// Here the graph holds the three kernels of one decode step (store_kv,
+// decode, merge).  Before each replay a small fill kernel (not captured: the
+// live batch size changes between replays) turns rows [bs, bucket) into the
+// dummy request: seq_len 1, the caller's dummy page-table row, out_loc = the
+// sentinel slot, zero q / k / v rows.  Every padded row therefore writes the
+// same zero row into the sentinel slot and attends to it alone.
+
+#include <algorithm>
+#include <new>
+#include <vector>
+
+#include "msgl.h"
+#include "internal.hpp"
+
+struct msgl_decode_graph {
+  void* k_cache = nullptr;
+  void* v_cache = nullptr;
+  int64_t num_slots = 0;
+  int64_t cache_row_stride = 0;
+  const int32_t* page_table = nullptr;
+  int64_t pt_stride = 0;
+  int32_t hq = 0, hkv = 0, page_size = 1, max_bs = 0, max_seq_len = 0;
+  float sm_scale = 0.f;
+  int32_t dummy_row = 0, sentinel_slot = 0;
+  char* q = nullptr;
+  char* k_new = nullptr;
+  char* v_new = nullptr;
+  char* out = nullptr;
+  float* lse = nullptr;
+  int32_t* seq_lens = nullptr;
+  int32_t* req_rows = nullptr;
+  int32_t* out_loc = nullptr;
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  std::vector<int32_t> ladder;          // ascending
+  std::vector<hipGraph_t> graphs;       // per ladder entry
+  std::vector<hipGraphExec_t> execs;
+};
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// rows [r0, r1) of the fixed buffers become the dummy request
+__global__ void __launch_bounds__(256) pad_rows_kernel(char* q, char* k_new, char* v_new,
+                                                       int32_t* seq_lens, int32_t* req_rows,
+                                                       int32_t* out_loc, int32_t r0, int32_t hq,
+                                                       int32_t hkv, int32_t dummy_row,
+                                                       int32_t sentinel) {
+  const int32_t r = r0 + (int32_t)blockIdx.x;
+  const int64_t qb = (int64_t)hq * 128 * 2;     // bytes of one q row
+  const int64_t kb = (int64_t)hkv * 128 * 2;    // bytes of one k / v row
+  const uint4 z = {0u, 0u, 0u, 0u};
+  for (int64_t o = 16 * (int64_t)threadIdx.x; o < qb; o += 16 * blockDim.x)
+    *reinterpret_cast<uint4*>(q + r * qb + o) = z;
+  for (int64_t o = 16 * (int64_t)threadIdx.x; o < kb; o += 16 * blockDim.x) {
+    *reinterpret_cast<uint4*>(k_new + r * kb + o) = z;
+    *reinterpret_cast<uint4*>(v_new + r * kb + o) = z;
+  }
+  if (threadIdx.x == 0) {
+    seq_lens[r] = 1;
+    req_rows[r] = dummy_row;
+    out_loc[r] = sentinel;
+  }
+}
+
+hipError_t pad(const msgl_decode_graph* g, int32_t r0, int32_t r1, hipStream_t s) {
+  if (r1 <= r0) return hipSuccess;
+  hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)(r1 - r0)), dim3(256), 0, s, g->q, g->k_new,
+                     g->v_new, g->seq_lens, g->req_rows, g->out_loc, r0, g->hq, g->hkv,
+                     g->dummy_row, g->sentinel_slot);
+  return hipGetLastError();
+}
+
+// the captured step for a batch of bs rows
+int step(const msgl_decode_graph* g, int32_t bs, hipStream_t s) {
+  int st = msgl_store_kv(g->k_cache, g->v_cache, g->num_slots, g->cache_row_stride, g->k_new,
+                         g->v_new, (int64_t)g->hkv * 128, g->out_loc, MSGL_INDEX_I32, bs, g->hkv,
+                         128, MSGL_DTYPE_BF16, s);
+  if (st != MSGL_OK) return st;
+  return msgl_paged_decode(g->out, g->lse, g->q, (int64_t)g->hq * 128, g->k_cache, g->v_cache,
+                           g->num_slots, g->cache_row_stride, g->page_table, g->pt_stride,
+                           g->req_rows, g->seq_lens, bs, g->hq, g->hkv, 128, g->page_size,
+                           g->max_seq_len, g->sm_scale, 0, g->ws, g->ws_bytes, s);
+}
+
+void release(msgl_decode_graph* g) {
+  for (hipGraphExec_t e : g->execs)
+    if (e) (void)hipGraphExecDestroy(e);
+  for (hipGraph_t gr : g->graphs)
+    if (gr) (void)hipGraphDestroy(gr);
+  delete g;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msgl_decode_graph_layout(int32_t max_bs, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t max_seq_len, size_t* offsets) {
+  if (!offsets || max_bs < 1 || num_q_heads < 1 || num_kv_heads < 1 || head_dim != 128 ||
+      max_seq_len < 1)
+    return MSGL_ERR_SHAPE;
+  const size_t B = (size_t)max_bs;
+  const size_t sizes[9] = {
+      B * num_q_heads * 128 * 2,            // q
+      B * num_kv_heads * 128 * 2,           // k_new
+      B * num_kv_heads * 128 * 2,           // v_new
+      B * num_q_heads * 128 * 2,            // out
+      B * num_q_heads * 4,                  // lse
+      B * 4,                                // seq_lens
+      B * 4,                                // req_rows
+      B * 4,                                // out_loc
+      msgl_paged_decode_workspace_size(max_bs, num_q_heads, num_kv_heads, 128, max_seq_len, 0,
+                                        nullptr)};
+  size_t off = 0;
+  for (int i = 0; i < 9; ++i) {
+    offsets[i] = off;
+    off += align256(sizes[i]);
+  }
+  offsets[9] = off;
+  return MSGL_OK;
+}
+
+int msgl_decode_graph_create(void* k_cache, void* v_cache, int64_t num_slots,
+                             int64_t cache_row_stride, const int32_t* page_table,
+                             int64_t page_table_stride, int32_t num_q_heads, int32_t num_kv_heads,
+                             int32_t head_dim, int32_t page_size, int32_t max_bs,
+                             int32_t max_seq_len, float sm_scale, int32_t dummy_row,
+                             int32_t sentinel_slot, void* buffer, size_t buffer_bytes,
+                             msgl_decode_graph** out) {
+  if (!out) return MSGL_ERR_NULL;
+  *out = nullptr;
+  if (!k_cache || !v_cache || !page_table || !buffer) return MSGL_ERR_NULL;
+  size_t off[10];
+  int st = msgl_decode_graph_layout(max_bs, num_q_heads, num_kv_heads, head_dim, max_seq_len, off);
+  if (st != MSGL_OK) return st;
+  if (buffer_bytes < off[9]) return MSGL_ERR_WORKSPACE;
+  if (((uintptr_t)buffer & 255) != 0) return MSGL_ERR_ALIGN;
+  if (dummy_row < 0 || sentinel_slot < 0 || sentinel_slot >= num_slots) return MSGL_ERR_SHAPE;
+
+  msgl_decode_graph* g = new (std::nothrow) msgl_decode_graph();
+  if (!g) return MSGL_ERR_LAUNCH;
+  g->k_cache = k_cache;
+  g->v_cache = v_cache;
+  g->num_slots = num_slots;
+  g->cache_row_stride = cache_row_stride;
+  g->page_table = page_table;
+  g->pt_stride = page_table_stride;
+  g->hq = num_q_heads;
+  g->hkv = num_kv_heads;
+  g->page_size = page_size;
+  g->max_bs = max_bs;
+  g->max_seq_len = max_seq_len;
+  g->sm_scale = sm_scale;
+  g->dummy_row = dummy_row;
+  g->sentinel_slot = sentinel_slot;
+  char* b = (char*)buffer;
+  g->q = b + off[0];
+  g->k_new = b + off[1];
+  g->v_new = b + off[2];
+  g->out = b + off[3];
+  g->lse = (float*)(b + off[4]);
+  g->seq_lens = (int32_t*)(b + off[5]);
+  g->req_rows = (int32_t*)(b + off[6]);
+  g->out_loc = (int32_t*)(b + off[7]);
+  g->ws = off[9] > off[8] ? (void*)(b + off[8]) : nullptr;
+  g->ws_bytes = off[9] - off[8];
+  for (int32_t s : {1, 2, 4})
+    if (s < max_bs) g->ladder.push_back(s);
+  for (int32_t s = 8; s < max_bs; s += 8) g->ladder.push_back(s);
+  g->ladder.push_back(max_bs);
+
+  // capture on a private stream (default priority), largest batch first
+  hipStream_t s = nullptr;
+  if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) != hipSuccess) {
+    release(g);
+    return MSGL_ERR_LAUNCH;
+  }
+  st = MSGL_OK;
+  g->graphs.assign(g->ladder.size(), nullptr);
+  g->execs.assign(g->ladder.size(), nullptr);
+  if (pad(g, 0, max_bs, s) != hipSuccess) st = MSGL_ERR_LAUNCH;
+  for (int i = (int)g->ladder.size() - 1; i >= 0 && st == MSGL_OK; --i) {
+    const int32_t bs = g->ladder[i];
+    st = step(g, bs, s);              // eager warm-up (also validates every argument)
+    if (st != MSGL_OK) break;
+    if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+      st = MSGL_ERR_LAUNCH;
+      break;
+    }
+    const int cst = step(g, bs, s);
+    hipGraph_t gr = nullptr;
+    const hipError_t e = hipStreamEndCapture(s, &gr);
+    g->graphs[i] = gr;
+    if (cst != MSGL_OK || e != hipSuccess || !gr) {
+      st = cst != MSGL_OK ? cst : MSGL_ERR_LAUNCH;
+      break;
+    }
+    if (hipGraphInstantiate(&g->execs[i], gr, nullptr, nullptr, 0) != hipSuccess) {
+      st = MSGL_ERR_LAUNCH;
+      break;
+    }
+  }
+  if (hipStreamSynchronize(s) != hipSuccess && st == MSGL_OK) st = MSGL_ERR_LAUNCH;
+  (void)hipStreamDestroy(s);
+  if (st != MSGL_OK) {
+    release(g);
+    return st;
+  }
+  *out = g;
+  return MSGL_OK;
+}
+
+int msgl_decode_graph_run(msgl_decode_graph* g, int32_t batch, hipStream_t stream) {
+  if (!g) return MSGL_ERR_NULL;
+  if (batch < 0 || batch > g->max_bs) return MSGL_ERR_SHAPE;
+  if (batch == 0) return MSGL_OK;
+  const size_t i = std::lower_bound(g->ladder.begin(), g->ladder.end(), batch) - g->ladder.begin();
+  if (pad(g, batch, g->ladder[i], stream) != hipSuccess) return MSGL_ERR_LAUNCH;
+  if (hipGraphLaunch(g->execs[i], stream) != hipSuccess) return MSGL_ERR_LAUNCH;
+  return MSGL_OK;
+}
+
+int32_t msgl_decode_graph_bucket(const msgl_decode_graph* g, int32_t batch) {
+  if (!g || batch < 1 || batch > g->max_bs) return -1;
+  return *std::lower_bound(g->ladder.begin(), g->ladder.end(), batch);
+}
+
+void msgl_decode_graph_destroy(msgl_decode_graph* g) {
+  if (g) release(g);
+}
+
+}  // extern "C"
