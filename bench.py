@@ -19,6 +19,7 @@ from __future__ import annotations
 import argparse
 import hashlib
 import json
+import math
 import os
 import platform
 import sys
@@ -54,6 +55,9 @@ WORKLOAD_TEXT = {
     "KVC": "host KV cache manager (page allocator + radix prefix cache, C++): 1,024 requests, "
            "each one of 32 Zipf(1.1)-popular 1,024-token system prompts + 128..256 own tokens, "
            "32..64 decode steps, page_size 16, 262,144-slot pool, 128 rows, seed 7",
+    "GRAPH": "decode step (store_kv + paged decode) replayed from captured HIP graphs vs eager "
+             "planned calls: Hq 32 / Hkv 8 / D 128, kv lens U[512,4096], 524,288-slot pool, "
+             "batch 1 / 8 / 32 / 64 of a 64-bucket ladder [1,2,4,8,16,...,64], seed 43",
     "EMB": "embedding gather: 8,192 token ids uniform over a 151,936 x 4,096 bf16 table "
            "(Qwen3-8B-class vocabulary and hidden size, one tensor-parallel rank), ids int32, "
            "table N(0,1), seed 41",
@@ -430,6 +434,57 @@ def kvcache_run():
                              "sample": "first 128 requests of the same trace"}}
 
 
+def graph_run(steps: int, warmup: int):
+    """Per-step time of store_kv + paged_decode at small batches: eager planned
+    calls against the graph runner (padding launch + graph replay)."""
+    import torch
+    import paged_kv_attention_30_amd as msgl
+    g = torch.Generator(device="cuda").manual_seed(43)
+    S, HQ, HKV, D, MAXB, W = 524288, 32, 8, 128, 64, 4096
+    k = torch.randn((S, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    v = torch.randn((S, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    perm = torch.randperm(S - 1, generator=g, device="cuda").to(torch.int32)
+    table = torch.zeros((MAXB + 1, W), dtype=torch.int32, device="cuda")
+    table[:MAXB] = perm[:MAXB * W].view(MAXB, W)
+    table[MAXB, 0] = S - 1
+    lens = torch.randint(512, 4097, (MAXB,), generator=g, device="cuda", dtype=torch.int32)
+    rows = torch.arange(MAXB, dtype=torch.int32, device="cuda")
+    loc = table[rows.long(), (lens - 1).long()].contiguous()
+    q = torch.randn((MAXB, HQ, D), generator=g, device="cuda").to(torch.bfloat16)
+    kn = torch.randn((MAXB, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    vn = torch.randn((MAXB, HKV, D), generator=g, device="cuda").to(torch.bfloat16)
+    scale = 1.0 / math.sqrt(D)
+    runner = msgl.DecodeGraph(k, v, table, HQ, MAXB, W, scale, MAXB, S - 1)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(steps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    res = {}
+    for bs in (1, 8, 32, 64):
+        ps = msgl.plan_store_kv(k, v, kn[:bs], vn[:bs], loc[:bs])
+        pd = msgl.plan_paged_decode(q[:bs], k, v, table, lens[:bs], W, scale, req_rows=rows[:bs])
+        eager = timed(lambda: (ps.run(), pd.run()))
+        runner.q[:bs].copy_(q[:bs]); runner.k_new[:bs].copy_(kn[:bs]); runner.v_new[:bs].copy_(vn[:bs])
+        runner.seq_lens[:bs].copy_(lens[:bs]); runner.req_rows[:bs].copy_(rows[:bs])
+        runner.out_loc[:bs].copy_(loc[:bs])
+        graph = timed(lambda: runner.run(bs))
+        res[str(bs)] = {"bucket": runner.bucket(bs), "eager_ms": round(eager, 4),
+                        "graph_ms": round(graph, 4)}
+    runner.close()
+    del k, v
+    return {"workload": WORKLOAD_TEXT["GRAPH"], "per_batch": res}
+
+
 def decode_figures(inp, res, steps):
     from workloads import metrics
     kv = metrics.decode_kv_bytes(inp.page_table, inp.dec_req_rows, inp.dec_seq_lens,
@@ -520,6 +575,9 @@ def main(argv=None) -> int:
         return 0
     if args.only == "PRO":
         print(json.dumps({"only": "PRO", **prologue_run(args.steps, args.warmup)}))
+        return 0
+    if args.only == "GRAPH":
+        print(json.dumps({"only": "GRAPH", **graph_run(args.steps, args.warmup)}))
         return 0
     if args.only:
         inp_o = make_config(args.only)

@@ -50,6 +50,7 @@ namespace msgl {
 namespace {
 
 constexpr int kTile = 32;          // keys per inner iteration
+constexpr int kMinKeysPerBlock = 128;   // balanced mode: fewest keys a working workgroup takes
 constexpr int kVtPitch = 32;       // LDS elements per head-dim row of V^T
 // LDS elements of one wave: its V^T tile, then a 128-byte slot for the
 // per-column (max, sum) a paired wave hands over
@@ -391,8 +392,10 @@ decode_balanced_kernel(DecodeParams p) {
     tl += ((int64_t)hi << 32) | (uint32_t)lo;
   }
   const int64_t T = uniform64(tl);
-  // with fewer keys than workgroups, only the first T workgroups take keys
-  const int64_t G = min((int64_t)Ggrid, T);
+  // every workgroup that takes keys takes at least kMinKeysPerBlock of them
+  // (a small batch cut into a few-key range per workgroup would spend its time
+  // in start-up latency and in merging hundreds of parts); the rest exit
+  const int64_t G = min((int64_t)Ggrid, max((int64_t)1, (T + kMinKeysPerBlock - 1) / kMinKeysPerBlock));
   // (64-bit division runs on the vector unit; move the results back to
   // scalar registers)
   const int64_t start = uniform64((G > 0 && b < G) ? (int64_t)b * T / G : T);
