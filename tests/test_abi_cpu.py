@@ -232,3 +232,26 @@ def test_embedding_gather_validation(lib):
     assert gather(w=None) == NULL
     assert gather(out=FAKE + 1) == ALIGN
     assert gather(idx=1, ids=FAKE + 4) == ALIGN
+
+
+def test_decode_graph_layout_rule(lib):
+    """The graph runner's buffer layout (host-only): regions in the documented
+    order, 256-byte aligned, each large enough, the decode workspace last."""
+    import ctypes
+    off = (ctypes.c_size_t * 10)()
+    assert lib.msgl_decode_graph_layout(64, 32, 8, 128, 4096, off) == OK
+    o = list(off)
+    need = [64 * 32 * 128 * 2, 64 * 8 * 128 * 2, 64 * 8 * 128 * 2, 64 * 32 * 128 * 2, 64 * 32 * 4,
+            64 * 4, 64 * 4, 64 * 4,
+            binding.paged_decode_workspace_size(64, 32, 8, 4096)[0]]
+    for i in range(9):
+        assert o[i] % 256 == 0
+        assert o[i + 1] - o[i] >= need[i]
+    assert lib.msgl_decode_graph_layout(0, 32, 8, 128, 4096, off) == SHAPE
+    assert lib.msgl_decode_graph_layout(4, 32, 8, 64, 4096, off) == SHAPE
+    assert lib.msgl_decode_graph_layout(4, 32, 8, 128, 4096, None) == SHAPE
+    h = ctypes.c_void_p()
+    assert lib.msgl_decode_graph_create(None, None, 0, 0, None, 0, 32, 8, 128, 1, 4, 64, 0.1, 0, 0,
+                                        None, 0, ctypes.byref(h)) == NULL
+    assert lib.msgl_decode_graph_run(None, 1, None) == NULL
+    assert lib.msgl_decode_graph_bucket(None, 1) == -1
