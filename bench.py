@@ -229,6 +229,28 @@ def timed_steps(run: Run, steps: int, warmup: int, graphs: bool = False):
                 dec_ms=[phase.get("decode", 0.0)], ext_ms=[phase.get("extend", 0.0)])
 
 
+def step_distribution(run: Run, steps: int):
+    """Median and p10 / p90 of single steps, each between its own pair of HIP
+    events and followed by a synchronisation (so each includes the event and
+    launch latency that the back-to-back figure leaves out)."""
+    torch = run.torch
+    calls = dict(run.phases())
+    order = [c for c in ("store", "decode", "extend") if c in calls]
+    ts = []
+    for _ in range(steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for c in order:
+            calls[c]()
+        b.record()
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b))
+    p10, p50, p90 = np.percentile(ts, [10, 50, 90])
+    return {"single_step_ms_p10": round(float(p10), 4), "single_step_ms_median": round(float(p50), 4),
+            "single_step_ms_p90": round(float(p90), 4)}
+
+
 def cold_decode_ms(run: Run, reps: int = 10):
     """Decode time with L2 and the 256 MB Infinity Cache flushed before each call.
 
@@ -597,6 +619,8 @@ def main(argv=None) -> int:
     value = kv / step_s / 1e9
     if not args.no_cold:
         head["decode_ms_cold_l2_mall_flushed"] = round(cold_decode_ms(run), 4)
+
+    head.update(step_distribution(run, args.steps))
 
     khash = kernel_hash()
     traffic = load_traffic(khash)
