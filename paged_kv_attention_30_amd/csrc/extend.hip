@@ -121,13 +121,19 @@ __device__ __forceinline__ int v_off(int t, int cg) {
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
+// m0 (the LDS base of these loads) is saved and restored around them, so the
+// compiler's view of it never changes.
 __device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_addr(lds_base)) : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_addr(lds_base)) : "memory");
 }
 __device__ __forceinline__ void dma4(const void* src, const void* lds_base) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(lds_addr(lds_base)) : "memory", "m0");
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_addr(lds_base)) : "memory");
 }
 
 constexpr int kWaves = 8;          // two groups of four: one wave of each group per SIMD
