@@ -69,8 +69,8 @@ int msgl_kvc_free_row(msgl_kv_cache* kvc, int32_t row);
 /* Longest page-aligned prefix of ids[0, n) held by the tree (§4.4.5): nodes
  * matched in full get a new LRU time, a node matched in part is split.
  * *cached_len = the prefix length, *handle = the node ending it (0: none).
- * With row >= 0 (a row holding no pages yet) the prefix's slots are written
- * to page_table[row, 0 .. *cached_len).  Does not lock. */
+ * With row >= 0 (a row holding no pages yet; n <= max_len) the prefix's
+ * slots are written to page_table[row, 0 .. *cached_len).  Does not lock. */
 int msgl_kvc_match(msgl_kv_cache* kvc, const int32_t* ids, int64_t n, int32_t row,
                    int64_t* cached_len, int64_t* handle);
 

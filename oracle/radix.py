@@ -200,7 +200,7 @@ class KVCacheOracle:
 
     def match(self, ids, row: int = -1):
         """match_req: (status, cached_len, handle node)."""
-        if row >= 0 and (not self.row_used[row] or self.row_len[row] != 0):
+        if row >= 0 and (not self.row_used[row] or self.row_len[row] != 0 or len(ids) > self.max_len):
             return ERR_ARG, 0, None
         node, prefix = self._walk(ids, len(ids))
         if row >= 0:

@@ -301,14 +301,12 @@ int msgl_kvc_free_row(msgl_kv_cache* c, int32_t row) {
 int msgl_kvc_match(msgl_kv_cache* c, const int32_t* ids, int64_t n, int32_t row,
                    int64_t* cached_len, int64_t* handle) {
   if (!c || (n > 0 && !ids) || n < 0 || !cached_len || !handle) return MSGL_KVC_ERR_ARG;
-  if (row >= 0 && (!row_ok(c, row) || c->row_len[row] != 0)) return MSGL_KVC_ERR_ARG;
+  if (row >= 0 && (!row_ok(c, row) || c->row_len[row] != 0 || n > c->max_len))
+    return MSGL_KVC_ERR_ARG;
   try {
     int64_t prefix = 0;
     const int64_t node = walk(c, ids, n, &prefix);
-    if (row >= 0) {
-      if (prefix > c->max_len) return MSGL_KVC_ERR_ARG;
-      path_slots(c, node, c->table.data() + (size_t)row * c->max_len);
-    }
+    if (row >= 0) path_slots(c, node, c->table.data() + (size_t)row * c->max_len);
     *cached_len = prefix;
     *handle = node;
   } catch (...) {

@@ -172,6 +172,7 @@ def test_argument_errors_change_nothing():
     st, row = cc.alloc_row()
     assert cc.allocate([row], [0], [33]) == -1        # beyond max_len
     assert cc.allocate([row], [4], [2]) == -1         # device < cached
+    assert cc.match(list(range(33)), row)[0] == -1    # a prompt longer than the row
     assert cc.free_row(row) == 0
     assert (cc.page_table == before[0]).all() and list(cc.free_list()) == before[1]
     assert cc.stats()[:5] == before[2][:5]
