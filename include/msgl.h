@@ -252,7 +252,8 @@ int msgl_rope_cos_sin_cache(float* cache, int64_t max_position, int32_t rotary_d
  *              msgl_rope_cos_sin_cache
  *   out_loc    n distinct slots, int32 or int64 (index_dtype); not checked
  * head_dim must be 128, num_q_heads a multiple of num_kv_heads; rows, norm
- * weights and the table 16-byte aligned, row strides multiples of 8 elements.
+ * weights, the table and the pool planes 16-byte aligned, row strides (qkv,
+ * q_out and the pool's) multiples of 8 elements.
  * n == 0 is a no-op.
  */
 int msgl_qk_norm_rope_store(void* q_out, int64_t q_out_row_stride, void* k_cache, void* v_cache,

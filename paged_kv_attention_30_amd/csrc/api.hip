@@ -438,8 +438,11 @@ int msgl_qk_norm_rope_store(void* q_out, int64_t q_out_row_stride, void* k_cache
                  aligned(cos_sin_cache, 16) &&
                  aligned(out_loc, index_dtype == MSGL_INDEX_I64 ? 8 : 4),
              MSGL_ERR_ALIGN, "rows, weights and table 16-byte aligned, indices element aligned");
-  MSGL_CHECK(qkv_row_stride % 8 == 0 && q_out_row_stride % 8 == 0, MSGL_ERR_ALIGN,
-             "qkv and q_out row strides must be multiples of 8 elements (16 bytes)");
+  MSGL_CHECK(qkv_row_stride % 8 == 0 && q_out_row_stride % 8 == 0 && cache_row_stride % 8 == 0,
+             MSGL_ERR_ALIGN,
+             "qkv, q_out and pool row strides must be multiples of 8 elements (16 bytes)");
+  MSGL_CHECK(aligned(k_cache, 16) && aligned(v_cache, 16), MSGL_ERR_ALIGN,
+             "k_cache and v_cache must be 16-byte aligned");
 
   msgl::PrologueArgs a;
   a.q_out = q_out;

@@ -255,3 +255,29 @@ def test_decode_graph_layout_rule(lib):
                                         None, 0, ctypes.byref(h)) == NULL
     assert lib.msgl_decode_graph_run(None, 1, None) == NULL
     assert lib.msgl_decode_graph_bucket(None, 1) == -1
+
+
+def test_prologue_validation(lib):
+    def pro(**kw):
+        a = dict(q=FAKE, qs=32 * 128, k=FAKE, v=FAKE2, slots=1024, cs=8 * 128, qkv=FAKE,
+                 qkvs=48 * 128, qw=None, kw=None, eps=1e-6, pos=FAKE, cache=FAKE, maxpos=4096,
+                 loc=FAKE, idx=0, n=4, hq=32, hkv=8, d=128)
+        a.update(kw)
+        return lib.msgl_qk_norm_rope_store(a["q"], a["qs"], a["k"], a["v"], a["slots"], a["cs"],
+                                           a["qkv"], a["qkvs"], a["qw"], a["kw"], a["eps"], a["pos"],
+                                           a["cache"], a["maxpos"], a["loc"], a["idx"], a["n"],
+                                           a["hq"], a["hkv"], a["d"], None)
+    assert pro(n=0) == OK
+    assert pro(n=-1) == SHAPE
+    assert pro(idx=7) == UNSUP
+    assert pro(d=64) == UNSUP
+    assert pro(hq=24) == UNSUP
+    assert pro(qkvs=40 * 128) == SHAPE
+    assert pro(qs=16 * 128) == SHAPE
+    assert pro(maxpos=0) == SHAPE
+    assert pro(eps=-1.0) == SHAPE
+    assert pro(pos=None) == NULL
+    assert pro(q=FAKE + 8) == ALIGN
+    assert pro(qkvs=48 * 128 + 4) == ALIGN
+    assert pro(cs=8 * 128 + 4) == ALIGN          # pool rows must stay 16-byte aligned
+    assert pro(k=FAKE + 8) == ALIGN
