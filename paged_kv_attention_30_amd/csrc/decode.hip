@@ -51,6 +51,10 @@ namespace {
 
 constexpr int kTile = 32;          // keys per inner iteration
 constexpr int kMinKeysPerBlock = 128;   // balanced mode: fewest keys a working workgroup takes
+// balanced mode: a request segment costs its keys plus this start-up (q rows,
+// page-table entries and the first keys arrive one after the other before
+// any work overlaps them; measured ~6 us, about one 32-key tile of work)
+constexpr int kSegmentCost = 32;
 constexpr int kVtPitch = 32;       // LDS elements per head-dim row of V^T
 // LDS elements of one wave: its V^T tile, then a 128-byte slot for the
 // per-column (max, sum) a paired wave hands over
@@ -383,8 +387,13 @@ decode_balanced_kernel(DecodeParams p) {
   const int B = p.batch;
 
   // total keys of the batch (every wave computes it; it is tiny)
+  // total cost of the batch: every non-empty request costs its keys plus
+  // kSegmentCost, laid out as [start-up | keys] on one line
   int64_t tl = 0;
-  for (int i = lane; i < B; i += 64) tl += max(p.seq_lens[i], 0);
+  for (int i = lane; i < B; i += 64) {
+    const int Li = p.seq_lens[i];
+    tl += Li > 0 ? Li + kSegmentCost : 0;
+  }
 #pragma unroll
   for (int d = 32; d >= 1; d >>= 1) {
     const int lo = __builtin_amdgcn_ds_bpermute(((lane ^ d) << 2), (int)(uint32_t)(tl & 0xffffffff));
@@ -417,26 +426,28 @@ decode_balanced_kernel(DecodeParams p) {
       if (running > end || (running == end && !last)) break;
       const int i = base + lane;
       const int Li = i < B ? max(p.seq_lens[i], 0) : 0;
-      const int incl = wave_incl_scan(Li);
-      const int64_t c0 = running + (incl - Li);
+      const int Ci = Li > 0 ? Li + kSegmentCost : 0;
+      const int incl = wave_incl_scan(Ci);
+      const int64_t c0 = running + (incl - Ci);
       const int64_t c1 = running + incl;
       bool own;
       if (i >= B || i <= r_prev) own = false;
-      else if (Li > 0) own = c1 > start && c0 < end;
+      else if (Li > 0) own = c1 > start && c0 + kSegmentCost < end;   // meets the keys
       else own = (c0 >= start && c0 < end) || (last && c0 == T);
       const uint64_t mask = __ballot(own);
       if (mask) {
         const int bit = __builtin_ctzll(mask);
         r = base + bit;
         r1 = running + __builtin_amdgcn_readlane(incl, bit);
-        r0 = r1 - __builtin_amdgcn_readlane(Li, bit);
+        const int Lr = __builtin_amdgcn_readlane(Li, bit);
+        r0 = r1 - Lr;            // position of the request's first key (after its start-up)
         break;
       }
       running += __builtin_amdgcn_readlane(incl, 63);
     }
     if (r < 0) break;
     r_prev = r;
-    if (r1 == r0) {
+    if (r1 == r0) {             // an empty request
       if (par == 0) write_empty(p, r, g, lane & 15, lane >> 4);
       if (writer) {
         p.meta[2 * r] = -1;
