@@ -566,8 +566,8 @@ def main(argv=None) -> int:
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the attention shards by request or kv head with no exchange; see the design notes)",
+        print("bench.py measures one GPU only: the library has no multi-GPU path (the attention "
+              "shards by request or by kv head with no exchange between GPUs)",
               file=sys.stderr)
         return 2
 

@@ -26,7 +26,7 @@ Sources (five web pages about the mini-sglang inference engine):
   (yunpan.plus), cited as [DDMS], section on chunked prefill: every chunk of
   a long prompt reuses the KV of the chunks before it.
 
-Readings where the pages are silent (each is also listed in the design doc):
+Readings where the pages are silent:
 
 * scores are ``sm_scale * (q . k)`` with the natural exponential; no
   soft-cap, no ALiBi, no window;

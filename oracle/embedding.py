@@ -10,7 +10,7 @@ Source: "Mini-SGLang complete analysis" (blog.rzhang-lab.cn):
     dimension across tensor-parallel ranks and combined by masked indexing
     followed by an all-reduce.
 
-Reading (also listed in the design doc): a rank holding vocabulary rows
+Reading: a rank holding vocabulary rows
 ``[vocab_start, vocab_start + rows)`` writes, for token id ``t``, row
 ``t - vocab_start`` of its table when ``t`` falls in that range and a row of
 zeros otherwise, so that the sum over ranks (the all-reduce) is the full

@@ -12,7 +12,7 @@ Source: "Mini-SGLang complete analysis" (blog.rzhang-lab.cn):
   - §4.5.6, one RoPE instance (one cos/sin cache of max_position x
     rotary_dim) is shared by every layer.
 
-Readings where the pages are silent (also listed in the design doc):
+Readings where the pages are silent:
   * RMSNorm of a head vector x (length D) with weight w:
     ``x / sqrt(mean(x^2) + eps) * w`` (eps = 1e-6 in the workloads);
   * RoPE rotates the pairs (x[i], x[i + D/2]) ("rotate half") by the angle

@@ -26,7 +26,7 @@ Source: "Mini-SGLang complete analysis" (blog.rzhang-lab.cn), §4.4:
 "Mini-sglang deep-analysis report" (nightvoyager.top), KV cache management:
 protected / evictable / free.
 
-Readings where the pages are silent or garbled (also listed in the design doc):
+Readings where the pages are silent or garbled:
   * the free list holds whole pages (the first slot of each) in FIFO order;
   * time is a logical clock, one tick per walk; leaves with equal times are
     evicted in node creation order;
