@@ -529,6 +529,13 @@ def summarize(name, inp, run, res, steps):
     step_ms = res["total_ms"] / steps
     d["ms_per_step"] = round(step_ms, 4)
     d["store_ms"] = round(float(np.mean(res["store_ms"])), 4)
+    # store_kv moves each new K and V row in and out once, plus its int64 index
+    n_new = int(inp.out_loc.shape[0])
+    store_bytes = 4 * n_new * inp.num_kv_heads * 128 * 2 + 8 * n_new
+    d["store_rows"] = n_new
+    d["store_GBps"] = round(store_bytes / (d["store_ms"] * 1e-3) / 1e9, 1) if d["store_ms"] > 0 else None
+    d["store_hbm_frac"] = (round(store_bytes / (d["store_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                           if d["store_ms"] > 0 else None)
     if inp.num_decode:
         kv, alg, dec_ms = decode_figures(inp, res, steps)
         d["decode_ms"] = round(dec_ms, 4)
