@@ -6,6 +6,7 @@ multiples, empty work).  Bars: store_kv and indexing invariants bit-exact;
 attention within max abs 2e-2 and max abs / max |ref| 1e-2.
 """
 
+import dataclasses
 import math
 import sys
 
@@ -15,7 +16,7 @@ import torch
 
 import oracle
 import paged_kv_attention_30_amd as msgl
-from workloads import small_decode, small_extend, random_bf16, config_c1
+from workloads import small_decode, small_extend, random_bf16, config_c1, f32_to_bf16_bits
 from tests.gpu_util import (Uploaded, up, bits, f64, assert_close, assert_lse_close)
 
 pytestmark = pytest.mark.gpu
@@ -414,6 +415,56 @@ def test_extend_negative_scale():
     ro, rl = oracle_extend(inp, kp, vp)
     assert_close(out, ro, "extend negative scale")
     assert_lse_close(lse, rl, "extend negative scale lse")
+
+
+def growing_scores(inp, sign, grow=0.2, seed=0):
+    """The same batch with every request's keys rebuilt so that scaled scores
+    rise by about ``grow`` log2 units per key position (q entries are shifted
+    to mean 2, K rows carry sign * g * position plus noise).  Every 64-key
+    tile then holds a new maximum more than 8 log2 units above the last one,
+    so the online softmax has to rescale its running sum and output on every
+    tile of every request, extend and decode alike."""
+    rng = np.random.default_rng(seed)
+    kp, _ = oracle_pool(inp)
+    kf = oracle.bf16_to_f64(kp)
+    c = abs(inp.sm_scale) * math.log2(math.e)
+    g = grow / (c * 2.0 * inp.head_dim)
+    spans = [(int(r), int(p) + int(e)) for r, p, e in
+             zip(inp.ext_req_rows, inp.ext_prefix_lens, inp.ext_extend_lens)]
+    spans += [(int(r), int(n)) for r, n in zip(inp.dec_req_rows, inp.dec_seq_lens)]
+    for row, n in spans:
+        slots = inp.page_table[row, :n]
+        t = np.arange(n, dtype=np.float64)[:, None, None]
+        kf[slots] = sign * g * t + 0.3 * rng.standard_normal((n,) + kf.shape[1:])
+    kbits = f32_to_bf16_bits(kf.astype(np.float32))
+    shift = lambda q: None if q is None else f32_to_bf16_bits(
+        (oracle.bf16_to_f64(q) + 2.0).astype(np.float32))
+    return dataclasses.replace(inp, k_pool=kbits, k_new=kbits[inp.out_loc],
+                               ext_q=shift(inp.ext_q), dec_q=shift(inp.dec_q))
+
+
+@pytest.mark.parametrize("scale", [0.0884, -0.09])
+def test_scores_growing_along_keys_rescale_every_tile(scale):
+    banner(f"growing scores, sm_scale={scale}")
+    base = small_extend(96, 32, 8, [(130, 70), (0, 200), (64, 1)], num_slots=4096,
+                        decode_lens=(150, 300, 33), sm_scale=scale)
+    inp = growing_scores(base, 1.0 if scale > 0 else -1.0)
+    u = Uploaded(inp)
+    u.store()
+    eo, el = u.extend()
+    do, dl = u.decode()
+    do_fixed, _ = u.decode(split_tokens=64)
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle_extend(inp, kp, vp)
+    # the weights really are concentrated near each row's last visible key
+    assert float(rl.max()) > 20.0
+    assert_close(eo, ro, "extend, growing scores")
+    assert_lse_close(el, rl, "extend lse, growing scores")
+    ro, rl = oracle_decode(inp, kp, vp)
+    assert_close(do, ro, "decode, growing scores")
+    assert_close(do_fixed, ro, "decode (fixed chunks), growing scores")
+    assert_lse_close(dl, rl, "decode lse, growing scores")
 
 
 def test_extend_with_shared_prefix_and_page_size_16():
