@@ -68,6 +68,16 @@ __device__ __forceinline__ float shfl_xor(float v, int mask) {
   return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
 }
 
+// max(v, v of lane l ^ 32) without the LDS crossbar: v_permlane32_swap of
+// (v, v) exchanges the lower half-wave of one copy with the upper half-wave
+// of the other, so in every lane the two results are v itself and the value
+// of lane l ^ 32 (which of the two comes first depends on the half).
+__device__ __forceinline__ float max_xor32(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
 // ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i
 // receives element i % 4 of the 8-byte rows addressed by lanes 4k + i / 4
 // (k = 0..3), i.e. a 16x4 block of 16-bit values comes back transposed.

@@ -199,12 +199,16 @@ paged_extend_kernel(ExtendParams p) {
   const int vis_end = P + qpos + 1;          // keys [0, vis_end) are visible
 
   // q as the B operand: column = query row, k-slot (jh, e) of step kk <->
-  // head dim 16*kk + 8*jh + e
+  // head dim 16*kk + 8*jh + e.  A negative scale is applied as a sign flip
+  // of q (exact in bf16, and every product and partial sum of the MFMA
+  // flips sign with it under round-to-nearest-even), so the scores below
+  // are always scaled by |scale|.
   u32x4 qb[8];
   {
     const uint16_t* qr = p.q + (int64_t)(qoff + qpos) * p.q_stride + (int64_t)head * kHeadDim;
+    const uint32_t qsign = p.scale_log2 < 0.f ? 0x80008000u : 0u;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qb[kk] = ld16(qr + 16 * kk + 8 * jh);
+    for (int kk = 0; kk < 8; ++kk) qb[kk] = ld16(qr + 16 * kk + 8 * jh) ^ qsign;
     // q is in registers before the look-ahead loads start (a wait the
     // compiler sees, so it adds none inside the tile loop)
     __builtin_amdgcn_s_waitcnt(0);
@@ -265,7 +269,7 @@ paged_extend_kernel(ExtendParams p) {
     for (int i = 0; i < 16; ++i) acc[mb][i] = 0.f;
   float m_run = -INFINITY;   // reference maximum, log2 units
   float l_run = 0.f;         // this lane's share of the running sum
-  const float c = p.scale_log2;
+  const float c = fabsf(p.scale_log2);   // > 0 (the sign went into q)
 
   // the lowest visible-key bound among this wave's rows decides whether a
   // tile needs the causal mask
@@ -312,25 +316,16 @@ paged_extend_kernel(ExtendParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kt + 32 * kb2 + 8 * (i >> 2) + 4 * jh + (i & 3);
-          if (key >= vis_end) s[kb2][i] = c >= 0.f ? -INFINITY : INFINITY;
+          if (key >= vis_end) s[kb2][i] = -INFINITY;
         }
     }
     // tile maximum of c * s, in log2 units
     float ext = s[0][0];
-    if (c >= 0.f) {
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+    for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) ext = fmaxf(ext, s[kb2][i]);
-      ext = fmaxf(ext, shfl_xor(ext, 32));
-    } else {
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ext = fminf(ext, s[kb2][i]);
-      ext = fminf(ext, shfl_xor(ext, 32));
-    }
-    const float m_tile = c * ext;
+      for (int i = 0; i < 16; ++i) ext = fmaxf(ext, s[kb2][i]);
+    const float m_tile = c * max_xor32(ext);
     if (__any(m_tile > m_run + kRescaleSlack)) {
       const float m_new = fmaxf(m_run, m_tile);
       const float alpha = fast_exp2(m_run - m_new);
@@ -347,9 +342,8 @@ paged_extend_kernel(ExtendParams p) {
 #pragma unroll
       for (int e2 = 0; e2 < 4; ++e2) {
         const int i0 = 8 * (u & 1) + 2 * e2;
-        // a masked score is +-inf with the sign that makes c * s = -inf, and
-        // m_run is finite here (key 0 is visible to every row, and c != 0),
-        // so a masked key's weight comes out exactly 0
+        // a masked score is -inf and m_run is finite here (key 0 is visible
+        // to every row, and c > 0), so a masked key's weight is exactly 0
         const float p0 = fast_exp2(fmaf(s[u >> 1][i0], c, -m_run));
         const float p1 = fast_exp2(fmaf(s[u >> 1][i0 + 1], c, -m_run));
         pb[u][e2] = pack_bf16x2(p0, p1);
