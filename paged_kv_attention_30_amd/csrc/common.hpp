@@ -78,6 +78,14 @@ __device__ __forceinline__ float max_xor32(float v) {
   return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
 }
 
+// The same over lane pairs l, l ^ 16: v_permlane16_swap exchanges the odd
+// 16-lane rows of one copy with the even rows of the other.
+__device__ __forceinline__ float max_xor16(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  return fmaxf(v, fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+
 // ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, lane i
 // receives element i % 4 of the 8-byte rows addressed by lanes 4k + i / 4
 // (k = 0..3), i.e. a 16x4 block of 16-bit values comes back transposed.

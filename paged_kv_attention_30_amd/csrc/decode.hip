@@ -244,8 +244,7 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
     float mt = sv[0];
 #pragma unroll
     for (int i = 1; i < 8; ++i) mt = fmaxf(mt, sv[i]);
-    mt = fmaxf(mt, shfl_xor(mt, 16));
-    mt = fmaxf(mt, shfl_xor(mt, 32));
+    mt = max_xor32(max_xor16(mt));
     const float m_new = fmaxf(m_run, mt);
     const float alpha = fast_exp2(m_run - m_new);
     m_run = m_new;
