@@ -101,7 +101,7 @@ def upload(inp):
 class Run:
     """One workload on the GPU: uploads once, then enqueues steps."""
 
-    def __init__(self, inp, split_tokens: int = 0):
+    def __init__(self, inp, split_tokens: int = 0, fuse_store: bool = True):
         import torch
         import paged_kv_attention_30_amd as msgl
         self.torch, self.msgl, self.inp = torch, msgl, inp
@@ -123,9 +123,19 @@ class Run:
             self.ext_ws = msgl.alloc_workspace(msgl.paged_extend_workspace_size(
                 inp.num_extend, inp.num_q_heads, inp.num_kv_heads, t["e_max"], t["e_kv"]))
 
-        # validated and marshalled once; each phase is then one library call
+        # validated and marshalled once; each phase is then one library call.
+        # A decode-only batch (one new row per request) stores and decodes in
+        # one launch, as the attention layer's forward runs the two.
+        self.fused = bool(fuse_store and inp.num_decode and not inp.num_extend
+                          and inp.out_loc.shape[0] == inp.num_decode)
         self.p_store = msgl.plan_store_kv(t["k"], t["v"], t["k_new"], t["v_new"], t["out_loc"])
-        if inp.num_decode:
+        if self.fused:
+            self.p_dec = msgl.plan_store_kv_paged_decode(
+                t["dq"], t["k"], t["v"], t["k_new"], t["v_new"], t["out_loc"], t["pt"],
+                t["d_lens"], t["d_max"], inp.sm_scale, req_rows=t["d_rows"],
+                page_size=inp.page_size, split_tokens=split_tokens, out=self.dec_out,
+                lse=self.dec_lse, workspace=self.ws)
+        elif inp.num_decode:
             self.p_dec = msgl.plan_paged_decode(
                 t["dq"], t["k"], t["v"], t["pt"], t["d_lens"], t["d_max"], inp.sm_scale,
                 req_rows=t["d_rows"], page_size=inp.page_size, split_tokens=split_tokens,
@@ -146,14 +156,15 @@ class Run:
         self.p_ext.run()
 
     def step(self):
-        self.store()
+        if not self.fused:
+            self.store()
         if self.inp.num_decode:
             self.decode()
         if self.inp.num_extend:
             self.extend()
 
     def phases(self):
-        ph = [("store", self.store)]
+        ph = [] if self.fused else [("store", self.store)]
         if self.inp.num_decode:
             ph.append(("decode", self.decode))
         if self.inp.num_extend:
@@ -225,7 +236,7 @@ def timed_steps(run: Run, steps: int, warmup: int, graphs: bool = False):
         b.record()
         torch.cuda.synchronize()
         phase[c] = a.elapsed_time(b) / steps
-    return dict(total_ms=total_ms, wall_s=wall, store_ms=[phase["store"]],
+    return dict(total_ms=total_ms, wall_s=wall, store_ms=[phase.get("store", 0.0)],
                 dec_ms=[phase.get("decode", 0.0)], ext_ms=[phase.get("extend", 0.0)])
 
 
@@ -507,12 +518,22 @@ def graph_run(steps: int, warmup: int):
     return {"workload": WORKLOAD_TEXT["GRAPH"], "per_batch": res}
 
 
-def decode_figures(inp, res, steps):
+def store_bytes_of(inp):
+    """store_kv moves each new K and V row in and out once, plus its int64 index."""
+    n_new = int(inp.out_loc.shape[0])
+    return 4 * n_new * inp.num_kv_heads * 128 * 2 + 8 * n_new
+
+
+def decode_figures(inp, res, steps, fused=False):
+    """KV bytes, algorithmic bytes and mean duration of one decode call (with
+    the store's bytes when the store runs in the same launch)."""
     from workloads import metrics
     kv = metrics.decode_kv_bytes(inp.page_table, inp.dec_req_rows, inp.dec_seq_lens,
                                  inp.num_kv_heads, 128)
     alg = metrics.decode_bytes(inp.page_table, inp.dec_req_rows, inp.dec_seq_lens,
                                inp.num_q_heads, inp.num_kv_heads, 128)
+    if fused:
+        alg += store_bytes_of(inp)
     dec_ms = float(np.mean(res["dec_ms"]))
     return kv, alg, dec_ms
 
@@ -528,16 +549,19 @@ def summarize(name, inp, run, res, steps):
     d = {"workload": WORKLOAD_TEXT.get(name, name)}
     step_ms = res["total_ms"] / steps
     d["ms_per_step"] = round(step_ms, 4)
-    d["store_ms"] = round(float(np.mean(res["store_ms"])), 4)
-    # store_kv moves each new K and V row in and out once, plus its int64 index
     n_new = int(inp.out_loc.shape[0])
-    store_bytes = 4 * n_new * inp.num_kv_heads * 128 * 2 + 8 * n_new
+    store_bytes = store_bytes_of(inp)
     d["store_rows"] = n_new
-    d["store_GBps"] = round(store_bytes / (d["store_ms"] * 1e-3) / 1e9, 1) if d["store_ms"] > 0 else None
-    d["store_hbm_frac"] = (round(store_bytes / (d["store_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+    if run.fused:
+        d["store"] = "in the decode launch (msgl_store_kv_paged_decode)"
+    else:
+        d["store_ms"] = round(float(np.mean(res["store_ms"])), 4)
+        d["store_GBps"] = (round(store_bytes / (d["store_ms"] * 1e-3) / 1e9, 1)
                            if d["store_ms"] > 0 else None)
+        d["store_hbm_frac"] = (round(store_bytes / (d["store_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+                               if d["store_ms"] > 0 else None)
     if inp.num_decode:
-        kv, alg, dec_ms = decode_figures(inp, res, steps)
+        kv, alg, dec_ms = decode_figures(inp, res, steps, run.fused)
         d["decode_ms"] = round(dec_ms, 4)
         d["decode_kv_gb"] = round(kv / 1e9, 4)
         d["decode_kv_GBps"] = round(kv / (dec_ms * 1e-3) / 1e9, 1)
@@ -562,6 +586,8 @@ def main(argv=None) -> int:
     ap.add_argument("--configs", default="C3,EMB,PRO",
                     help="extra workloads (comma list of C3,C4,C5a,C5b,EMB,PRO; '' for none)")
     ap.add_argument("--split-tokens", type=int, default=0)
+    ap.add_argument("--separate-store", action="store_true",
+                    help="decode-only batches: store_kv and the decode as two launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--graphs", action="store_true",
@@ -610,18 +636,18 @@ def main(argv=None) -> int:
         return 0
     if args.only:
         inp_o = make_config(args.only)
-        run_o = Run(inp_o, args.split_tokens)
+        run_o = Run(inp_o, args.split_tokens, not args.separate_store)
         res_o = timed_steps(run_o, args.steps, args.warmup, args.graphs)
         print(json.dumps({"only": args.only, **summarize(args.only, inp_o, run_o, res_o, args.steps)}))
         return 0
 
     log("generating the headline decode batch")
     inp = make_config("C2")
-    run = Run(inp, args.split_tokens)
+    run = Run(inp, args.split_tokens, not args.separate_store)
     log(f"timing {args.steps} steps after {args.warmup} warm-up steps")
     res = timed_steps(run, args.steps, args.warmup, args.graphs)
     head = summarize("C2", inp, run, res, args.steps)
-    kv, alg, dec_ms = decode_figures(inp, res, args.steps)
+    kv, alg, dec_ms = decode_figures(inp, res, args.steps, run.fused)
     step_s = res["total_ms"] * 1e-3 / args.steps
     value = kv / step_s / 1e9
     if not args.no_cold:
@@ -635,8 +661,11 @@ def main(argv=None) -> int:
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": "decode_balanced_kernel<8, 2> + merge_kernel (one msgl_paged_decode call)",
+                "kernel": ("decode_balanced_kernel<8, 2> (store_kv fused) + merge_kernel "
+                           "(one msgl_store_kv_paged_decode call)" if run.fused else
+                           "decode_balanced_kernel<8, 2> + merge_kernel (one msgl_paged_decode call)"),
                 "alg_bytes_per_launch": alg, "avg_launch_ms": round(dec_ms, 4)}
+    fused = run.fused
     del run
     torch.cuda.empty_cache()
 
@@ -649,7 +678,7 @@ def main(argv=None) -> int:
             torch.cuda.empty_cache()
             continue
         inp_x = make_config(name)
-        run_x = Run(inp_x, args.split_tokens)
+        run_x = Run(inp_x, args.split_tokens, not args.separate_store)
         res_x = timed_steps(run_x, max(5, args.steps // 5), 3, args.graphs)
         extras[name] = summarize(name, inp_x, run_x, res_x, max(5, args.steps // 5))
         del run_x
@@ -673,7 +702,10 @@ def main(argv=None) -> int:
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_TEXT["C2"], "step": "store_kv(64 rows) + paged_decode (+LSE merge)",
+        "config": {"workload": WORKLOAD_TEXT["C2"],
+                   "step": ("store_kv(64 rows) + paged_decode (+LSE merge) in one "
+                            "msgl_store_kv_paged_decode launch + the merge" if fused else
+                            "store_kv(64 rows) + paged_decode (+LSE merge)"),
                    "split_tokens": head.get("decode_split_tokens"), "page_size": 1,
                    "launch": "hip_graph_replay" if args.graphs else "planned_calls"},
         "roofline": roofline,

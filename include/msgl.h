@@ -12,6 +12,9 @@
  *                      [same page, §1.2 (decode is memory-bound), §1.4 (paged
  *                      pool + per-request page table), §4.5.3 (GQA ratio),
  *                      §4.6.4 (table kept at page_size 1)]
+ *   msgl_store_kv_paged_decode  the two above in one launch, as the
+ *                      attention layer's forward runs them back to back
+ *                      ["Mini-SGLang complete analysis" §4.6.7]
  *   msgl_paged_extend  causal chunked-prefill attention over a cached prefix
  *                      plus the chunk itself
  *                      ["Deep dive into mini-sglang: chunked prefill and
@@ -143,6 +146,34 @@ int msgl_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_st
                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                       int32_t max_seq_len, float sm_scale, int32_t split_tokens,
                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * msgl_store_kv_paged_decode — msgl_store_kv of one new row per request
+ * followed by msgl_paged_decode, in one launch ("Mini-SGLang complete
+ * analysis" §4.6.7: the attention layer's forward stores the step's K/V and
+ * then attends over the pool, so the newest key of every request is the row
+ * just stored).  Row r of k_new / v_new ([batch, row] elements, row r at
+ * r * new_row_stride, 16-byte aligned rows) is request r's new token: it is
+ * written to slot out_loc[r] (int32 or int64 per index_dtype), and the
+ * attention takes key seq_lens[r] - 1 of request r from that row directly,
+ * so no part of the launch reads a slot another part is writing.
+ * The caller guarantees out_loc[r] == page_table[row, seq_lens[r] - 1] for
+ * every request with seq_lens[r] > 0 (the allocator's contract); then the
+ * pool and the outputs are bit-identical to msgl_store_kv(n = batch)
+ * followed by msgl_paged_decode with the same arguments.  Every other
+ * argument, the workspace and the errors are those of the two calls
+ * (k_new / v_new rows must also be 16-byte aligned: MSGL_ERR_ALIGN).
+ */
+int msgl_store_kv_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_stride,
+                               void* k_cache, void* v_cache, int64_t num_slots,
+                               int64_t cache_row_stride, const void* k_new, const void* v_new,
+                               int64_t new_row_stride, const void* out_loc, int32_t index_dtype,
+                               const int32_t* page_table, int64_t page_table_stride,
+                               const int32_t* req_rows, const int32_t* seq_lens, int32_t batch,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t page_size, int32_t max_seq_len, float sm_scale,
+                               int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream);
 
 /* Bytes of workspace msgl_paged_decode needs for these host-side sizes
  * (0 if no request can need more than one chunk).  The split size actually

@@ -9,11 +9,13 @@ from .binding import (  # noqa: F401
     PlannedCall,
     plan_store_kv,
     plan_paged_decode,
+    plan_store_kv_paged_decode,
     plan_paged_extend,
     load,
     version,
     store_kv,
     paged_decode,
+    store_kv_paged_decode,
     paged_decode_workspace_size,
     paged_extend,
     paged_extend_workspace_size,

@@ -40,6 +40,11 @@ SIGNATURES = {
                                  _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p, _i32, _i32,
                                  _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p, _size_t,
                                  _c_void_p]),
+    "msgl_store_kv_paged_decode": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
+                                          _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64,
+                                          _c_void_p, _i32, _c_void_p, _i64, _c_void_p,
+                                          _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                          _i32, _c_void_p, _size_t, _c_void_p]),
     "msgl_paged_decode_workspace_size": (_size_t, [_i32, _i32, _i32, _i32, _i32, _i32,
                                                    ctypes.POINTER(_i32)]),
     "msgl_paged_extend": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p,
@@ -253,6 +258,65 @@ def plan_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       workspace: torch.Tensor | None = None) -> PlannedCall:
     """Planned form of :func:`paged_decode`; ``run()`` returns ``(out, lse)``."""
     lib = load()
+    d = _decode_args(q, k_cache, v_cache, page_table, seq_lens, max_seq_len, sm_scale, req_rows,
+                     page_size, split_tokens, out, lse, want_lse, workspace)
+    return PlannedCall(lib.msgl_paged_decode, d["args"], "msgl_paged_decode", d["outputs"],
+                       d["keep"])
+
+
+def store_kv_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                          k_new: torch.Tensor, v_new: torch.Tensor, out_loc: torch.Tensor,
+                          page_table: torch.Tensor, seq_lens: torch.Tensor, max_seq_len: int,
+                          sm_scale: float, req_rows: torch.Tensor | None = None,
+                          page_size: int = 1, split_tokens: int = 0,
+                          out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                          want_lse: bool = True, workspace: torch.Tensor | None = None,
+                          stream=None):
+    """store_kv of one new row per request, then decode, in one launch.
+
+    Row r of ``k_new`` / ``v_new`` [B, Hkv, 128] is request r's newest token;
+    it goes to slot ``out_loc[r]``, which must be ``page_table[row_r,
+    seq_lens[r] - 1]``.  Returns ``(out, lse)`` like :func:`paged_decode`.
+    """
+    return plan_store_kv_paged_decode(q, k_cache, v_cache, k_new, v_new, out_loc, page_table,
+                                      seq_lens, max_seq_len, sm_scale, req_rows, page_size,
+                                      split_tokens, out, lse, want_lse, workspace).run(stream)
+
+
+def plan_store_kv_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                               k_new: torch.Tensor, v_new: torch.Tensor, out_loc: torch.Tensor,
+                               page_table: torch.Tensor, seq_lens: torch.Tensor,
+                               max_seq_len: int, sm_scale: float,
+                               req_rows: torch.Tensor | None = None, page_size: int = 1,
+                               split_tokens: int = 0, out: torch.Tensor | None = None,
+                               lse: torch.Tensor | None = None, want_lse: bool = True,
+                               workspace: torch.Tensor | None = None) -> PlannedCall:
+    """Planned form of :func:`store_kv_paged_decode`."""
+    lib = load()
+    d = _decode_args(q, k_cache, v_cache, page_table, seq_lens, max_seq_len, sm_scale, req_rows,
+                     page_size, split_tokens, out, lse, want_lse, workspace)
+    B, hkv, dim = q.shape[0], k_cache.shape[1], k_cache.shape[2]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t, torch.bfloat16, name, 3)
+        if tuple(t.shape) != (B, hkv, dim) or t.stride(2) != 1 or t.stride(1) != dim:
+            raise ValueError(f"{name} must be [B, Hkv, D] with heads x dims contiguous")
+    if k_new.stride(0) != v_new.stride(0):
+        raise ValueError("k_new and v_new must share a row stride")
+    if out_loc.dtype not in (torch.int32, torch.int64) or not out_loc.is_cuda:
+        raise TypeError("out_loc must be an int32 or int64 GPU tensor")
+    if out_loc.dim() != 1 or out_loc.shape[0] != B or not out_loc.is_contiguous():
+        raise ValueError("out_loc must be a contiguous [B] vector")
+    a = d["args"]
+    # (out, lse, q, q_stride, k, v, slots, cstride) + new rows + (page_table ...)
+    args = (*a[:8], _ptr(k_new), _ptr(v_new), k_new.stride(0), _ptr(out_loc),
+            INDEX_I64 if out_loc.dtype == torch.int64 else INDEX_I32, *a[8:])
+    return PlannedCall(lib.msgl_store_kv_paged_decode, args, "msgl_store_kv_paged_decode",
+                       d["outputs"], (*d["keep"], k_new, v_new, out_loc))
+
+
+def _decode_args(q, k_cache, v_cache, page_table, seq_lens, max_seq_len, sm_scale, req_rows,
+                 page_size, split_tokens, out, lse, want_lse, workspace):
+    """Checks and marshals the arguments shared by the decode entry points."""
     _need(q, torch.bfloat16, "q", 3)
     n_slots, hkv, d, cstride = _pool_geometry(k_cache, v_cache)
     B, hq, dq = q.shape
@@ -287,8 +351,8 @@ def plan_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
             cstride, _ptr(page_table), page_table.stride(0), _ptr(req_rows), _ptr(seq_lens), B, hq,
             hkv, d, page_size, max_seq_len, float(sm_scale), split_tokens, _ptr(workspace),
             ws_bytes)
-    return PlannedCall(lib.msgl_paged_decode, args, "msgl_paged_decode", (out, lse),
-                       (q, k_cache, v_cache, page_table, seq_lens, req_rows, workspace))
+    return {"args": args, "outputs": (out, lse),
+            "keep": (q, k_cache, v_cache, page_table, seq_lens, req_rows, workspace)}
 
 
 # ---------------------------------------------------------------------------

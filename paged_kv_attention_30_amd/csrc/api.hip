@@ -189,14 +189,26 @@ size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads, int3
   return decode_workspace(batch, num_q_heads, head_dim, max_seq_len, split_tokens).total();
 }
 
-int msgl_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_stride,
+namespace {
+
+// The new rows a fused store+decode call writes (null: a plain decode).
+struct FusedStore {
+  const void* k_new;
+  const void* v_new;
+  int64_t new_row_stride;
+  const void* out_loc;
+  int32_t index_dtype;
+};
+
+int paged_decode_impl(void* out, float* lse_out, const void* q, int64_t q_row_stride,
                       const void* k_cache, const void* v_cache, int64_t num_slots,
                       int64_t cache_row_stride, const int32_t* page_table,
                       int64_t page_table_stride, const int32_t* req_rows,
                       const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                       int32_t max_seq_len, float sm_scale, int32_t split_tokens,
-                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                      void* workspace, size_t workspace_bytes, const FusedStore* fs,
+                      hipStream_t stream, const char* where) {
   g_last_error[0] = 0;
   MSGL_CHECK(batch >= 0, MSGL_ERR_SHAPE, "batch %d is negative", batch);
   int st = validate_pool(k_cache, v_cache, num_slots, cache_row_stride, num_kv_heads, head_dim);
@@ -229,7 +241,27 @@ int msgl_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_st
   MSGL_CHECK(need == 0 || (workspace && aligned(workspace, 256)), MSGL_ERR_WORKSPACE,
              "workspace must be non-NULL and 256-byte aligned");
 
+  if (fs) {
+    MSGL_CHECK(fs->index_dtype == MSGL_INDEX_I32 || fs->index_dtype == MSGL_INDEX_I64,
+               MSGL_ERR_UNSUPPORTED, "index dtype %d unsupported", fs->index_dtype);
+    MSGL_CHECK(fs->new_row_stride >= (int64_t)num_kv_heads * head_dim, MSGL_ERR_SHAPE,
+               "new_row_stride %lld < num_kv_heads*head_dim", (long long)fs->new_row_stride);
+    MSGL_CHECK(fs->k_new && fs->v_new && fs->out_loc, MSGL_ERR_NULL,
+               "k_new, v_new and out_loc must be non-NULL");
+    MSGL_CHECK(aligned(fs->k_new, 16) && aligned(fs->v_new, 16) && (fs->new_row_stride * 2) % 16 == 0,
+               MSGL_ERR_ALIGN, "k_new / v_new rows must be 16-byte aligned");
+    MSGL_CHECK(aligned(fs->out_loc, fs->index_dtype == MSGL_INDEX_I64 ? 8 : 4), MSGL_ERR_ALIGN,
+               "out_loc must be aligned to its element size");
+  }
+
   msgl::DecodeArgs a;
+  a.k_store = fs ? const_cast<void*>(k_cache) : nullptr;
+  a.v_store = fs ? const_cast<void*>(v_cache) : nullptr;
+  a.k_new = fs ? fs->k_new : nullptr;
+  a.v_new = fs ? fs->v_new : nullptr;
+  a.new_stride = fs ? fs->new_row_stride : 0;
+  a.out_loc = fs ? fs->out_loc : nullptr;
+  a.out_loc_is_i64 = fs && fs->index_dtype == MSGL_INDEX_I64;
   a.out = out;
   a.lse = lse_out;
   a.q = q;
@@ -260,7 +292,42 @@ int msgl_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_st
     a.balanced_blocks = device_compute_units();
     a.max_splits = 0;
   }
-  return launch_status(msgl::launch_paged_decode(a), "paged_decode");
+  return launch_status(msgl::launch_paged_decode(a), where);
+}
+
+}  // namespace
+
+int msgl_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_stride,
+                      const void* k_cache, const void* v_cache, int64_t num_slots,
+                      int64_t cache_row_stride, const int32_t* page_table,
+                      int64_t page_table_stride, const int32_t* req_rows,
+                      const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                      int32_t max_seq_len, float sm_scale, int32_t split_tokens,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return paged_decode_impl(out, lse_out, q, q_row_stride, k_cache, v_cache, num_slots,
+                           cache_row_stride, page_table, page_table_stride, req_rows, seq_lens,
+                           batch, num_q_heads, num_kv_heads, head_dim, page_size, max_seq_len,
+                           sm_scale, split_tokens, workspace, workspace_bytes, nullptr, stream,
+                           "paged_decode");
+}
+
+int msgl_store_kv_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_stride,
+                               void* k_cache, void* v_cache, int64_t num_slots,
+                               int64_t cache_row_stride, const void* k_new, const void* v_new,
+                               int64_t new_row_stride, const void* out_loc, int32_t index_dtype,
+                               const int32_t* page_table, int64_t page_table_stride,
+                               const int32_t* req_rows, const int32_t* seq_lens, int32_t batch,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               int32_t page_size, int32_t max_seq_len, float sm_scale,
+                               int32_t split_tokens, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  const FusedStore fs{k_new, v_new, new_row_stride, out_loc, index_dtype};
+  return paged_decode_impl(out, lse_out, q, q_row_stride, k_cache, v_cache, num_slots,
+                           cache_row_stride, page_table, page_table_stride, req_rows, seq_lens,
+                           batch, num_q_heads, num_kv_heads, head_dim, page_size, max_seq_len,
+                           sm_scale, split_tokens, workspace, workspace_bytes, &fs, stream,
+                           "store_kv_paged_decode");
 }
 
 size_t msgl_paged_extend_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -96,6 +96,39 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// s_waitcnt with only the vector-memory counter constrained (<= n).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 16, "vmcnt immediate");
+  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(n) : "memory");
+}
+
+// Direct global -> LDS loads, issued from inline assembly so the compiler
+// neither tracks them nor inserts waits for them: callers order them with
+// explicit vmcnt waits (vector-memory loads complete in order).
+// Each wave instruction fills LDS at the wave-uniform base, lane l at
+// +size*l.
+// (The base must be the same in every lane; it is moved to a scalar
+// register, which costs nothing when the compiler already knows it uniform.)
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+}
+// m0 (the LDS base of these loads) is saved and restored around them, so the
+// compiler's view of it never changes.
+__device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_addr(lds_base)) : "memory");
+}
+__device__ __forceinline__ void dma4(const void* src, const void* lds_base) {
+  uint32_t saved;
+  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\t"
+               "s_mov_b32 m0, %0"
+               : "=&s"(saved) : "v"(src), "s"(lds_addr(lds_base)) : "memory");
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

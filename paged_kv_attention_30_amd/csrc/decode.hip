@@ -26,16 +26,20 @@
 //   split_tokens = S > 0: chunk c of request r is keys [cS, (c+1)S), one
 //   workgroup per (chunk, request).)
 // * Keys are processed 32 at a time.  Each lane fetches the page-table entry
-//   of "its" token and issues 16-byte loads of that token's K and V row
-//   segment (a wave reads 64 contiguous bytes per token per instruction).
+//   of "its" token and issues 16-byte loads of that token's K row segment
+//   into registers (a wave reads 64 contiguous bytes per token per
+//   instruction); the tile's V rows go straight from HBM into the wave's LDS
+//   tile (global_load_lds_dwordx4, 1 KiB per wave instruction), so they hold
+//   no registers on the way.
 // * S^T = K Q^T runs on the 16x16x32 bf16 MFMA: K rows go straight from the
 //   loads into the A operand (row = token), q heads of the group are the
 //   B operand columns (ratio <= 16, unused columns are zero).  The output
 //   layout gives every lane one q head, so running max / sum / rescale are
 //   per-lane scalars; the max needs two cross-lane steps.
 // * O^T = V^T P^T also runs on MFMA: P^T is the QK output repacked to bf16
-//   in place (its C layout is exactly the B layout of the next MFMA), and V^T
-//   is staged through a wave-private LDS tile written transposed.
+//   in place (its C layout is exactly the B layout of the next MFMA), and the
+//   V^T operand comes from the key-major V tile through the transposing LDS
+//   read (ds_read_b64_tr_b16).
 // * Reduction order depends only on logical key positions and lengths, so
 //   results are bit-identical under any slot permutation and for any
 //   page_size.
@@ -55,10 +59,9 @@ constexpr int kMinKeysPerBlock = 128;   // balanced mode: fewest keys a working 
 // page-table entries and the first keys arrive one after the other before
 // any work overlaps them; measured ~6 us, about one 32-key tile of work)
 constexpr int kSegmentCost = 32;
-constexpr int kVtPitch = 32;       // LDS elements per head-dim row of V^T
-// LDS elements of one wave: its V^T tile, then a 128-byte slot for the
+// LDS elements of one wave: its V tile, then a 128-byte slot for the
 // per-column (max, sum) a paired wave hands over
-constexpr int kWaveLds = kHeadDim * kVtPitch + 64;
+constexpr int kWaveLds = kTile * kHeadDim + 64;
 
 struct DecodeParams {
   uint16_t* out;
@@ -81,14 +84,58 @@ struct DecodeParams {
   float* part_out;        // [slots, Hq, 128]
   float* part_lse;        // [slots, Hq]
   int32_t* meta;          // balanced mode: per request (first, last) workgroup
+  // Store fused into the launch (k_store null: none).  Row r of k_new /
+  // v_new is request r's newest token, stored at slot out_loc[r], which is
+  // key seq_lens[r] - 1 of the request; the attention takes that key from
+  // the new row itself, so no workgroup reads a slot another one writes.
+  char* k_store;
+  char* v_store;
+  const char* k_new;
+  const char* v_new;
+  int64_t new_stride_bytes;
+  const void* out_loc;
+  int32_t out_loc_i64;
+  int32_t row_units;      // 16-byte units of one K (or V) row
 };
 
-// position of key t (0..31 of a tile) inside a V^T row: the B-operand slot
-// (l / 16, e) of the PV MFMA stands for key 4*(l/16) + e (e < 4) or
-// 16 + 4*(l/16) + (e - 4) (e >= 4), i.e. the keys the QK output left in lane l.
-__device__ __forceinline__ int vt_pos(int t) {
-  return 8 * ((t & 15) >> 2) + 4 * (t >> 4) + (t & 3);
+// The lane index, hidden from loop-invariant code motion: per-lane addresses
+// of the rarely taken paths below are then formed where they are used
+// instead of being hoisted out of the segment loop into registers (and
+// spilled, as the tile loop needs all of them).
+__device__ __forceinline__ int lane_here() {
+  int l = __lane_id();
+  asm volatile("" : "+v"(l));
+  return l;
 }
+
+// The fused store, one kv head's slice of request r's new row: lanes 0-15
+// carry the 256 bytes of K, lanes 16-31 those of V, one 16-byte unit each.
+// new_slice loads them; store_slice writes them to slot out_loc[r].
+__device__ __forceinline__ u32x4 new_slice(const DecodeParams& p, int r, int g) {
+  const int lane = lane_here();
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (lane < 32)
+    v = ld16((lane < 16 ? p.k_new : p.v_new) + (int64_t)r * p.new_stride_bytes +
+             (int64_t)g * kHeadDim * 2 + 16 * (lane & 15));
+  return v;
+}
+
+__device__ __forceinline__ void store_slice(const DecodeParams& p, int r, int g, u32x4 v) {
+  const int lane = lane_here();
+  const int64_t slot = p.out_loc_i64 ? reinterpret_cast<const int64_t*>(p.out_loc)[r]
+                                     : (int64_t)reinterpret_cast<const int32_t*>(p.out_loc)[r];
+  if (lane < 32)
+    st16((lane < 16 ? p.k_store : p.v_store) + slot * p.cache_stride_bytes +
+             (int64_t)g * kHeadDim * 2 + 16 * (lane & 15),
+         v);
+}
+
+// A wave's V tile: key-major rows of 128 dims (256 bytes); the 8-byte group
+// g (dims 4g .. 4g+3) of key t sits at group position g ^ 4 (t & 7).  A
+// transposed read takes 8 keys (t & 7 distinct) x 4 consecutive groups per
+// 32 lanes; the XOR spreads them over all 32 group positions of a 256-byte
+// bank row, so the read is free of bank conflicts, and it keeps together the
+// group pairs a 16-byte direct load writes.
 
 __device__ __forceinline__ int shfl_up_i(int v, int d) {
   const int lane = __lane_id();
@@ -114,7 +161,9 @@ __device__ __forceinline__ int64_t uniform64(int64_t v) {
 }
 
 // Output of an empty request: zeros and lse = -inf.
-__device__ __forceinline__ void write_empty(const DecodeParams& p, int r, int g, int c, int j) {
+__device__ __forceinline__ void write_empty(const DecodeParams& p, int r, int g) {
+  const int lane = lane_here();
+  const int c = lane & 15, j = lane >> 4;
   if (c >= p.ratio) return;
   const int h = g * p.ratio + c;
   uint16_t* o = p.out + ((int64_t)r * p.num_q_heads + h) * kHeadDim;
@@ -127,18 +176,23 @@ __device__ __forceinline__ void write_empty(const DecodeParams& p, int r, int g,
 // One wave: attention of request r's q heads of kv head g over keys
 // [t0, t1) (t0 < t1).  Writes the final bf16 output + lse when `whole`,
 // else the normalised fp32 partial + lse at partial row `slot`.
-// `vt` is the wave's V^T tile (128 x kVtPitch), `qs` its group's q rows
+// `vt` is the wave's V tile (32 keys x 128 dims), `qs` its group's q rows
 // (ratio x 128).  With NPAR = 2 two waves share the segment: wave `par`
 // takes the tiles t0 + 32 (2i + par); at the end the parity-1 wave leaves
-// its state in its V^T tile (`pvt` is that tile, seen from the pair) and the
+// its state in its V tile (`pvt` is that tile, seen from the pair) and the
 // parity-0 wave folds it in and writes the result.  Every wave of the
 // workgroup must call this for the same segments (it holds workgroup
 // barriers).
+// With the store fused, `last_key` is the request's newest key when this
+// segment holds it (else -1): the wave whose tiles include that key stores
+// the head's slice of the new row at the start of the segment and reads it
+// back from the pool like every other key (a wave sees its own stores once
+// they have completed), so no other wave or workgroup touches that slot.
 template <int NPAR>
 __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* vt,
                                                uint16_t* qs, uint16_t* pvt, int par, int r,
                                                int g, int t0, int t1, bool whole,
-                                               int64_t slot) {
+                                               int64_t slot, int last_key) {
   const int lane = __lane_id();
   const int c = lane & 15;      // q-head column / token row inside the MFMA
   const int j = lane >> 4;      // k-slot group
@@ -157,6 +211,11 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
     const int u = lane + 64 * k;
     if (u < R * 16) qv[k] = ld16(qg + 8 * u);
   }
+  // the wave whose tiles hold the newest key stores it (waves take tiles
+  // t0 + 32 (NPAR i + par))
+  const bool stores_new = last_key >= t0 && ((last_key - t0) / kTile) % NPAR == par;
+  u32x4 nv;
+  if (stores_new) nv = new_slice(p, r, g);
   // B operand of S^T = K Q^T: column c, k-slot (j, e) of step kk <-> head dim
   // 32*kk + 8*j + e.  Columns c >= ratio read a real row again; their output
   // columns are never used and MFMA columns do not mix.
@@ -164,9 +223,19 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
 
   const int64_t cs = p.cache_stride_bytes;
   const char* kbase = p.k_cache + (int64_t)g * kHeadDim * 2 + (8 * j) * 2;
-  const int64_t v_minus_k = p.v_cache - p.k_cache;   // same layout, other plane
-  const int pos_a = vt_pos(c);        // key c of the tile
-  const int pos_b = vt_pos(16 + c);   // key 16 + c
+  // V direct loads: this lane's key within each 4-key load and its physical
+  // 16-byte unit; transposed reads: lane 4k + q of each 16-lane group
+  // addresses key k of its run, 8-byte group q of the dim block
+  const int ld_key = lane >> 4;
+  const int bp_addr = 4 * ld_key;                           // lane ld_key, in bytes
+  const int uoff = 16 * ((lane & 15) ^ (2 * ld_key));       // unit bytes, load 0
+  // transposed reads: lane 4k + q of 16-lane group j addresses key
+  // tr_t = 4j + k, group q of the dim block (the byte offset of dim block mb
+  // is 32 mb ^ tr_sw within the row; the hi keys sit 16 rows = 4 KiB on)
+  const int tr_t = 4 * j + ((lane & 15) >> 2);
+  const int tr_base = 256 * tr_t + 8 * (lane & 3);
+  const int tr_sw = 32 * (tr_t & 7);
+  const char* vbase = p.v_cache + (int64_t)g * kHeadDim * 2;
 
   f32x4 acc[8];
 #pragma unroll
@@ -186,19 +255,34 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
     const int u = lane + 64 * k;
     if (u < R * 16) *reinterpret_cast<u32x4*>(qs + 8 * u) = qv[k];
   }
+  if (stores_new) store_slice(p, r, g, nv);
   __builtin_amdgcn_wave_barrier();
 
   for (int tb = tfirst; tb < t1; tb += kStep) {
+    // V tile: straight from HBM into this wave's LDS tile, key-major rows of
+    // 256 bytes.  Load i fills rows 4i .. 4i+3 (lane l: key 4i + l/16,
+    // physical 16-byte unit l % 16, holding logical unit (l % 16) ^ 2(key & 7),
+    // the tile layout above).  A lane takes the slot of its key from the lane that holds
+    // it (keys c in na, 16 + c in nb).  The previous tile's V reads finished
+    // before its P V MFMAs, and every wave reads only its own tile.
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+    // the tile holding the newest key of a fused store: its row was stored
+    // by this wave at the start of the segment; wait until it has landed
+    // (the table entries of this tile, the only other loads in flight, are
+    // needed now anyway)
+    if ((unsigned)(last_key - tb) < (unsigned)kTile) wait_vmcnt<0>();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      // key 4i + ld_key: its slot sits in lane 4 (i % 4) + ld_key, and its
+      // swizzle 2 (key & 7) = 2 ld_key + 8 (i % 2) only flips unit bit 3
+      const int sl = __builtin_amdgcn_ds_bpermute(bp_addr + 16 * (i & 3), i < 4 ? na : nb);
+      const int uo = uoff ^ (128 * (i & 1));
+      dma16(vbase + (int64_t)sl * cs + uo, vt + 512 * i);
+    }
+    // K rows of keys c and 16 + c go to registers: the A operand of S^T = K Q^T
     const char* ra = kbase + (int64_t)na * cs;
     const char* rb = kbase + (int64_t)nb * cs;
-    // V first: it goes to LDS as soon as it lands, which frees its
-    // registers before the QK operands are needed
-    u32x4 va[4], vb[4], ka[4], kb[4];
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      va[kk] = ld16(ra + v_minus_k + 64 * kk);
-      vb[kk] = ld16(rb + v_minus_k + 64 * kk);
-    }
+    u32x4 ka[4], kb[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       ka[kk] = ld16(ra + 64 * kk);
@@ -208,22 +292,6 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
       na = pt[min(tb + kStep + c, t1 - 1)];
       nb = pt[min(tb + kStep + 16 + c, t1 - 1)];
     }
-
-    // V^T tile: lane holds V[key c][dims 32kk+8j .. +7] and V[key 16+c][...]
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int d = 32 * kk + 8 * j + 2 * e;
-        const uint32_t wa = va[kk][e];
-        const uint32_t wb = vb[kk][e];
-        vt[d * kVtPitch + pos_a] = (uint16_t)(wa & 0xffffu);
-        vt[(d + 1) * kVtPitch + pos_a] = (uint16_t)(wa >> 16);
-        vt[d * kVtPitch + pos_b] = (uint16_t)(wb & 0xffffu);
-        vt[(d + 1) * kVtPitch + pos_b] = (uint16_t)(wb >> 16);
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
 
     f32x4 s_a = {0.f, 0.f, 0.f, 0.f}, s_b = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -263,22 +331,36 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
     l_run = l_run * alpha + psum;
     const u32x4 pb = {pw[0], pw[1], pw[2], pw[3]};
 
+    // the V loads are older than the K loads and the table entries after
+    // them, so at most those two entries may still be in flight
+    wait_vmcnt<2>();
+    // V^T operand of dim block mb: lane (c, j) gets dims 16 mb + c of keys
+    // 4j .. 4j+3 and 16 + 4j .. 16 + 4j + 3 from two transposed reads, the
+    // k order of the P^T operand
+    // (the empty asm makes the swizzle look new every tile, so the eight
+    // addresses are formed here, two VALU ops each, rather than hoisted out
+    // of the loop into eight registers)
+    int sw = tr_sw;
+    asm volatile("" : "+v"(sw));
+    const char* vrow = reinterpret_cast<const char*>(vt) + tr_base;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
-      const u32x4 a = *reinterpret_cast<const u32x4*>(vt + (16 * mb + c) * kVtPitch + 8 * j);
+      const char* at = vrow + (sw ^ (32 * mb));
+      const u32x2 lo = lds_read_tr16(reinterpret_cast<const uint16_t*>(at));
+      const u32x2 hi = lds_read_tr16(reinterpret_cast<const uint16_t*>(at + 4096));
+      const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
       acc[mb] = acc[mb] * alpha;
       acc[mb] = mfma16x16x32(a, pb, acc[mb]);
     }
-    __builtin_amdgcn_wave_barrier();
   }
 
   float l_tot = l_run + shfl_xor(l_run, 16);
   l_tot += shfl_xor(l_tot, 32);
   if (NPAR > 1) {
-    // the parity-1 wave's state: acc as [mb][lane] f32x4 in its V^T tile,
+    // the parity-1 wave's state: acc as [mb][lane] f32x4 in its V tile,
     // (max, sum) per head column in the slot after it
     f32x4* xacc = reinterpret_cast<f32x4*>(pvt);
-    float* xml = reinterpret_cast<float*>(pvt + kHeadDim * kVtPitch);
+    float* xml = reinterpret_cast<float*>(pvt + kTile * kHeadDim);
     if (par == 1) {
 #pragma unroll
       for (int mb = 0; mb < 8; ++mb) xacc[mb * 64 + lane] = acc[mb];
@@ -330,7 +412,7 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
   }
 }
 
-// LDS of a workgroup with `nw` waves: the V^T tile (+ hand-over slot) of
+// LDS of a workgroup with `nw` waves: the V tile (+ hand-over slot) of
 // every wave, then the q rows of every kv-head group (shared by the waves of
 // a pair).
 __device__ __forceinline__ uint16_t* wave_vt(uint16_t* base, int w) {
@@ -345,7 +427,6 @@ template <int KVB>
 __global__ void __launch_bounds__(KVB * 64, 4)
 decode_fixed_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t dyn_lds[];
-  const int lane = threadIdx.x & 63;
   const int w = threadIdx.x >> 6;
   uint16_t* vt = wave_vt(dyn_lds, w);
   uint16_t* qs = group_qs(dyn_lds, KVB, w, p.ratio);
@@ -355,7 +436,10 @@ decode_fixed_kernel(DecodeParams p) {
   const int S = p.split_tokens;
   const int L = p.seq_lens[r];
   if (L <= 0) {
-    if (split == 0) write_empty(p, r, g, lane & 15, lane >> 4);
+    if (split == 0) {
+      write_empty(p, r, g);
+      if (p.k_store) store_slice(p, r, g, new_slice(p, r, g));
+    }
     return;
   }
   const int t0 = split * S;
@@ -364,7 +448,8 @@ decode_fixed_kernel(DecodeParams p) {
   // no chunk index ever exceeds the workspace
   const int nsplit = min((L + S - 1) / S, p.max_splits);
   const int t1 = (split == p.max_splits - 1) ? L : min(t0 + S, L);
-  attend_segment<1>(p, vt, qs, vt, 0, r, g, t0, t1, nsplit == 1, (int64_t)split * p.batch + r);
+  attend_segment<1>(p, vt, qs, vt, 0, r, g, t0, t1, nsplit == 1, (int64_t)split * p.batch + r,
+                    p.k_store && t1 == L ? L - 1 : -1);
 }
 
 // Balanced ranges: workgroup b of G owns flattened keys [b*T/G, (b+1)*T/G).
@@ -446,8 +531,11 @@ decode_balanced_kernel(DecodeParams p) {
     }
     if (r < 0) break;
     r_prev = r;
-    if (r1 == r0) {             // an empty request
-      if (par == 0) write_empty(p, r, g, lane & 15, lane >> 4);
+    if (r1 == r0) {             // an empty request (its new row is still stored)
+      if (par == 0) {
+        write_empty(p, r, g);
+        if (p.k_store) store_slice(p, r, g, new_slice(p, r, g));
+      }
       if (writer) {
         p.meta[2 * r] = -1;
         p.meta[2 * r + 1] = -1;
@@ -457,7 +545,8 @@ decode_balanced_kernel(DecodeParams p) {
     const int s0 = (int)(max(start, r0) - r0);
     const int s1 = (int)(min(end, r1) - r0);
     const bool whole = r0 >= start && r1 <= end;
-    attend_segment<NPAR>(p, vt, qs, pvt, par, r, g, s0, s1, whole, (int64_t)b + r);
+    attend_segment<NPAR>(p, vt, qs, pvt, par, r, g, s0, s1, whole, (int64_t)b + r,
+                         p.k_store && r1 <= end ? (int)(r1 - r0) - 1 : -1);
     if (writer) {
       // workgroups holding the first and the last key of request r
       const int64_t bf = ((r0 + 1) * G - 1) / T;
@@ -548,6 +637,14 @@ hipError_t launch_paged_decode(const DecodeArgs& a) {
   p.part_out = a.part_out;
   p.part_lse = a.part_lse;
   p.meta = a.meta;
+  p.k_store = (char*)a.k_store;
+  p.v_store = (char*)a.v_store;
+  p.k_new = (const char*)a.k_new;
+  p.v_new = (const char*)a.v_new;
+  p.new_stride_bytes = a.new_stride * 2;
+  p.out_loc = a.out_loc;
+  p.out_loc_i64 = a.out_loc_is_i64 ? 1 : 0;
+  p.row_units = a.num_kv_heads * kHeadDim * 2 / 16;
 
   hipError_t err;
   switch (decode_kv_heads_per_block(a.num_kv_heads)) {

@@ -48,13 +48,6 @@ constexpr int kPvDepth = 3;        // V^T operand reads in flight ahead of the P
 constexpr int kTileElems = kBN * kHeadDim;   // one K or V tile, bf16 elements
 constexpr int kPieces = kTileElems * 2 / 1024;  // 1-KiB LDS pieces per K (or V) tile
 
-// s_waitcnt with only the vector-memory counter constrained (<= n).
-template <int n>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(n >= 0 && n < 16, "vmcnt immediate");
-  asm volatile("s_waitcnt vmcnt(%0)" :: "n"(n) : "memory");
-}
-
 // Workgroup barrier without the memory fence __syncthreads() carries (that
 // fence waits for every outstanding load, including tiles meant to stay in
 // flight).  Callers order LDS themselves: every wave has waited for its own
@@ -111,29 +104,6 @@ __device__ __forceinline__ int k_off(int t, int chunk) {
 // keeps the 16-byte pairs a direct load writes together.
 __device__ __forceinline__ int v_off(int t, int cg) {
   return t * kHeadDim + 4 * (cg ^ (8 * (t & 3)));
-}
-
-// Direct global -> LDS loads, issued from inline assembly so the compiler
-// neither tracks them nor inserts waits for them: the loader below orders
-// them with explicit vmcnt waits (vector-memory loads complete in order).
-// Each wave instruction fills LDS at the wave-uniform base, lane l at
-// +size*l.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
-}
-// m0 (the LDS base of these loads) is saved and restored around them, so the
-// compiler's view of it never changes.
-__device__ __forceinline__ void dma16(const void* src, const void* lds_base) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %1, off\n\t"
-               "s_mov_b32 m0, %0"
-               : "=&s"(saved) : "v"(src), "s"(lds_addr(lds_base)) : "memory");
-}
-__device__ __forceinline__ void dma4(const void* src, const void* lds_base) {
-  uint32_t saved;
-  asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\tglobal_load_lds_dword %1, off\n\t"
-               "s_mov_b32 m0, %0"
-               : "=&s"(saved) : "v"(src), "s"(lds_addr(lds_base)) : "memory");
 }
 
 constexpr int kWaves = 8;          // two groups of four: one wave of each group per SIMD

@@ -89,6 +89,15 @@ struct DecodeArgs {
   float* part_out;         // fp32 [rows, Hq, 128]
   float* part_lse;         // fp32 [rows, Hq]
   int32_t* meta;           // balanced mode: int32 [B, 2]
+  // store fused into the decode launch (k_store null: none): row r of
+  // k_new / v_new (row stride new_stride elements) goes to slot out_loc[r]
+  void* k_store;
+  void* v_store;
+  const void* k_new;
+  const void* v_new;
+  int64_t new_stride;
+  const void* out_loc;
+  bool out_loc_is_i64;
   hipStream_t stream;
 };
 

@@ -100,6 +100,44 @@ def test_decode_empty_batch_is_a_no_op(lib):
     assert decode(lib, batch=0) == OK
 
 
+def fused(lib, **kw):
+    args = dict(out=FAKE, lse=FAKE, q=FAKE, q_stride=32 * 128, k=FAKE, v=FAKE2, slots=1024,
+                cstride=8 * 128, knew=FAKE, vnew=FAKE2, nstride=8 * 128, loc=FAKE, idx=0,
+                pt=FAKE, pt_stride=4096, rows=None, lens=FAKE, batch=4, hq=32, hkv=8, d=128,
+                page=1, max_len=4096, scale=0.088, split=0, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    a = args
+    return lib.msgl_store_kv_paged_decode(
+        a["out"], a["lse"], a["q"], a["q_stride"], a["k"], a["v"], a["slots"], a["cstride"],
+        a["knew"], a["vnew"], a["nstride"], a["loc"], a["idx"], a["pt"], a["pt_stride"],
+        a["rows"], a["lens"], a["batch"], a["hq"], a["hkv"], a["d"], a["page"], a["max_len"],
+        a["scale"], a["split"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(knew=None), NULL),
+    (dict(vnew=None), NULL),
+    (dict(loc=None), NULL),
+    (dict(knew=FAKE + 8), ALIGN),
+    (dict(nstride=8 * 128 + 4), ALIGN),
+    (dict(nstride=100), SHAPE),
+    (dict(idx=7), UNSUP),
+    (dict(loc=FAKE + 2), ALIGN),
+    (dict(idx=1, loc=FAKE + 4), ALIGN),
+    (dict(k=None), NULL),            # the decode's own checks come first
+    (dict(hq=24), UNSUP),
+    (dict(ws=None, ws_bytes=0), WS),
+])
+def test_store_decode_validation(lib, kw, code):
+    st = fused(lib, **kw)
+    assert st == code, (st, lib.msgl_last_error())
+    assert b"api.hip" in lib.msgl_last_error()
+
+
+def test_store_decode_empty_batch_is_a_no_op(lib):
+    assert fused(lib, batch=0) == OK
+
+
 def test_decode_workspace_size_rule(lib):
     # balanced ranges (split 0): partials for up to 2048 workgroups + batch
     n, s = msgl.paged_decode_workspace_size(64, 32, 8, 4096, 0)
