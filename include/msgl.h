@@ -157,10 +157,14 @@ int msgl_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_st
  * written to slot out_loc[r] (int32 or int64 per index_dtype), and the
  * attention takes key seq_lens[r] - 1 of request r from that row directly,
  * so no part of the launch reads a slot another part is writing.
- * The caller guarantees out_loc[r] == page_table[row, seq_lens[r] - 1] for
- * every request with seq_lens[r] > 0 (the allocator's contract); then the
- * pool and the outputs are bit-identical to msgl_store_kv(n = batch)
- * followed by msgl_paged_decode with the same arguments.  Every other
+ * The caller guarantees, for every request r with seq_lens[r] > 0, that
+ * out_loc[r] == page_table[row, seq_lens[r] - 1] and that no other request
+ * of the batch has out_loc[r] among its keys (the slot was just allocated
+ * for r's new token, as the pages' allocator does; shared prefix pages hold
+ * cached keys only).  Then the pool and the outputs are bit-identical to
+ * msgl_store_kv(n = batch) followed by msgl_paged_decode with the same
+ * arguments; otherwise another request may see the slot before or after
+ * the store.  Every other
  * argument, the workspace and the errors are those of the two calls
  * (k_new / v_new rows must also be 16-byte aligned: MSGL_ERR_ALIGN).
  */
@@ -337,8 +341,9 @@ int msgl_merge_states(void* out, float* lse_out, const float* part_out,
  *
  *   page_table[dummy_row, 0] must hold sentinel_slot, a slot no request owns
  *   (the pages reserve one extra page for it); padded rows all write zeros
- *   there, and so does create (its warm-up runs fully padded batches).  The pool, the page table and the buffer must stay at their
- *   addresses while the graph lives.
+ *   there, and so does create (its warm-up runs fully padded batches).  The
+ *   pool, the page table and the buffer must stay at their addresses while
+ *   the graph lives.
  * create: validates (same rules as the two calls), warms up and captures on a
  *   private stream, synchronises it; allocates the graphs (host/runtime
  *   objects) — a set-up call.  run: two launches (padding + graph), no

@@ -276,7 +276,8 @@ def store_kv_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch
 
     Row r of ``k_new`` / ``v_new`` [B, Hkv, 128] is request r's newest token;
     it goes to slot ``out_loc[r]``, which must be ``page_table[row_r,
-    seq_lens[r] - 1]``.  Returns ``(out, lse)`` like :func:`paged_decode`.
+    seq_lens[r] - 1]`` and no key of another request of the batch (a freshly
+    allocated slot).  Returns ``(out, lse)`` like :func:`paged_decode`.
     """
     return plan_store_kv_paged_decode(q, k_cache, v_cache, k_new, v_new, out_loc, page_table,
                                       seq_lens, max_seq_len, sm_scale, req_rows, page_size,

@@ -108,11 +108,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // explicit vmcnt waits (vector-memory loads complete in order).
 // Each wave instruction fills LDS at the wave-uniform base, lane l at
 // +size*l.
-// (The base must be the same in every lane; it is moved to a scalar
-// register, which costs nothing when the compiler already knows it uniform.)
+// (The base must be the same in every lane and known so to the compiler: it
+// goes into a scalar register.)
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(
-      (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p);
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
 // m0 (the LDS base of these loads) is saved and restored around them, so the
 // compiler's view of it never changes.

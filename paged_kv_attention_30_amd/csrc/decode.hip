@@ -212,7 +212,10 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
     if (u < R * 16) qv[k] = ld16(qg + 8 * u);
   }
   // the wave whose tiles hold the newest key stores it (waves take tiles
-  // t0 + 32 (NPAR i + par))
+  // t0 + 32 (NPAR i + par)).  That key is the last of the segment, so its
+  // tile is the segment's last one: the other wave's tiles all lie below it
+  // and never touch the slot, not even through the lanes a tail tile clamps
+  // to its last key.
   const bool stores_new = last_key >= t0 && ((last_key - t0) / kTile) % NPAR == par;
   u32x4 nv;
   if (stores_new) nv = new_slice(p, r, g);
@@ -427,7 +430,7 @@ template <int KVB>
 __global__ void __launch_bounds__(KVB * 64, 4)
 decode_fixed_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t dyn_lds[];
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
   uint16_t* vt = wave_vt(dyn_lds, w);
   uint16_t* qs = group_qs(dyn_lds, KVB, w, p.ratio);
   const int r = blockIdx.x % p.batch;
@@ -459,7 +462,7 @@ __global__ void __launch_bounds__(KVB * 64 * NPAR, 4)
 decode_balanced_kernel(DecodeParams p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t dyn_lds[];
   const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave index (uniform)
   const int wk = w % KVB;
   const int par = w / KVB;
   uint16_t* vt = wave_vt(dyn_lds, w);
