@@ -1,8 +1,8 @@
 """The page tables the host KV cache manager produces drive the attention
 kernels: store_kv at the slots it allocates, extend over a prefix it matched
-(shared pages of another request), decode steps on the rows it grows — each
-checked against the fp64 oracle on the same table, and page_size 16 against
-page_size 1 bit for bit.
+(shared pages of another request), decode steps on the rows it grows (every
+other step as one store + decode launch) — each checked against the fp64
+oracle on the same table, and page_size 16 against page_size 1 bit for bit.
 """
 
 import sys
@@ -73,7 +73,11 @@ def test_manager_page_tables_drive_store_extend_and_decode():
         assert kv.allocate(rows, lens, [x + 1 for x in lens]) == 0
         loc = np.array([kv.page_table[r, n] for r, n in zip(rows, lens)], np.int64)
         k_new, v_new = random_bf16(rng, (len(rows), HKV, D)), random_bf16(rng, (len(rows), HKV, D))
-        msgl.store_kv(k_dev, v_dev, up(k_new), up(v_new), up(loc))
+        # odd steps store and decode in one launch (the manager hands out fresh
+        # slots for the new tokens, the contract of the fused call)
+        fused = step % 2 == 1
+        if not fused:
+            msgl.store_kv(k_dev, v_dev, up(k_new), up(v_new), up(loc))
         kp, vp = oracle.store_kv(kp, vp, k_new, v_new, loc)
         for n in running:
             running[n][1].append(int(rng.integers(0, 1000)))
@@ -81,8 +85,14 @@ def test_manager_page_tables_drive_store_extend_and_decode():
         seq = np.array([x + 1 for x in lens], np.int32)
         q = random_bf16(rng, (len(rows), HQ, D))
         table = kv.page_table.copy()
-        o16, l16 = msgl.paged_decode(up(q), k_dev, v_dev, up(table), up(seq), int(seq.max()), SCALE,
-                                     req_rows=up(np.array(rows, np.int32)), page_size=P)
+        if fused:
+            o16, l16 = msgl.store_kv_paged_decode(
+                up(q), k_dev, v_dev, up(k_new), up(v_new), up(loc), up(table), up(seq),
+                int(seq.max()), SCALE, req_rows=up(np.array(rows, np.int32)), page_size=P)
+        else:
+            o16, l16 = msgl.paged_decode(up(q), k_dev, v_dev, up(table), up(seq), int(seq.max()),
+                                         SCALE, req_rows=up(np.array(rows, np.int32)),
+                                         page_size=P)
         o1, _ = msgl.paged_decode(up(q), k_dev, v_dev, up(table), up(seq), int(seq.max()), SCALE,
                                   req_rows=up(np.array(rows, np.int32)), page_size=1)
         torch.cuda.synchronize()
