@@ -4,11 +4,12 @@ A step is one pass of the path over one synthetic batch with every input
 already resident in HBM.  The headline workload is the 8B-class decode
 batch (Hq 32 / Hkv 8 / head_dim 128, 64 requests with kv lengths uniform
 in [512, 4096], a 512K-slot randomly permuted pool, page_size 1): a step is
-``store_kv`` of the 64 new K/V rows followed by the split-KV paged decode
-(decode kernel + LSE merge).  The line also carries the extend workload
-(8 chunked-prefill requests over prefixes up to 8K, 4 of them sharing one
-2,048-slot prefix) and, with ``--configs``, the long-tail and mixed-batch
-workloads.
+``store_kv`` of the 64 new K/V rows and the split-KV paged decode, run as
+one store + decode launch and the LSE merge.  The line also carries the
+other workloads (``--configs``, all of them by default): the extend batch (8
+chunked-prefill requests over prefixes up to 8K, 4 of them sharing one
+2,048-slot prefix), the long-tail decode batch, the mixed batch at page_size
+1 and 16, the embedding gather and the attention-layer prologue.
 
 Prints ONE JSON line (rank 0, N = 1).  ``value`` = distinct K/V bytes the
 decode must read / (wall time of the K timed steps / K).
@@ -583,7 +584,7 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--configs", default="C3,EMB,PRO",
+    ap.add_argument("--configs", default="C3,C4,C5a,C5b,EMB,PRO",
                     help="extra workloads (comma list of C3,C4,C5a,C5b,EMB,PRO; '' for none)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--separate-store", action="store_true",

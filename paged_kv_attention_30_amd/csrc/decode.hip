@@ -183,22 +183,22 @@ __device__ __forceinline__ void write_empty(const DecodeParams& p, int r, int g)
 // parity-0 wave folds it in and writes the result.  Every wave of the
 // workgroup must call this for the same segments (it holds workgroup
 // barriers).
-// With the store fused, `last_key` is the request's newest key when this
-// segment holds it (else -1): the wave whose tiles include that key stores
-// the head's slice of the new row at the start of the segment and reads it
-// back from the pool like every other key (a wave sees its own stores once
-// they have completed), so no other wave or workgroup touches that slot.
+// `row` is the request's page-table row.  With the store fused, `last_key`
+// is the request's newest key when this segment holds it (else -1): the
+// wave whose tiles include that key stores the head's slice of the new row
+// at the start of the segment and reads it back from the pool like every
+// other key (a wave sees its own stores once they have completed), so no
+// other wave or workgroup touches that slot.
 template <int NPAR>
 __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* vt,
                                                uint16_t* qs, uint16_t* pvt, int par, int r,
                                                int g, int t0, int t1, bool whole,
-                                               int64_t slot, int last_key) {
+                                               int64_t slot, int last_key, int row) {
   const int lane = __lane_id();
   const int c = lane & 15;      // q-head column / token row inside the MFMA
   const int j = lane >> 4;      // k-slot group
   const int R = p.ratio;
 
-  const int row = p.req_rows ? p.req_rows[r] : r;
   const int32_t* pt = p.page_table + (int64_t)row * p.pt_stride;
 
   // q rows of the group (ratio x 128 bf16) are loaded now and parked in LDS
@@ -226,12 +226,13 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
 
   const int64_t cs = p.cache_stride_bytes;
   const char* kbase = p.k_cache + (int64_t)g * kHeadDim * 2 + (8 * j) * 2;
-  // V direct loads: this lane's key within each 4-key load and its physical
-  // 16-byte unit; transposed reads: lane 4k + q of each 16-lane group
-  // addresses key k of its run, 8-byte group q of the dim block
+  // V direct loads: this lane's key within each 4-key load (ld_key), the
+  // byte address of the lane holding that key's slot, and the byte offset of
+  // the 16-byte unit it fetches for load 0 (its physical unit lane % 16 holds
+  // logical unit (lane % 16) ^ 2 (key & 7))
   const int ld_key = lane >> 4;
-  const int bp_addr = 4 * ld_key;                           // lane ld_key, in bytes
-  const int uoff = 16 * ((lane & 15) ^ (2 * ld_key));       // unit bytes, load 0
+  const int bp_addr = 4 * ld_key;
+  const int uoff = 16 * ((lane & 15) ^ (2 * ld_key));
   // transposed reads: lane 4k + q of 16-lane group j addresses key
   // tr_t = 4j + k, group q of the dim block (the byte offset of dim block mb
   // is 32 mb ^ tr_sw within the row; the hi keys sit 16 rows = 4 KiB on)
@@ -452,7 +453,7 @@ decode_fixed_kernel(DecodeParams p) {
   const int nsplit = min((L + S - 1) / S, p.max_splits);
   const int t1 = (split == p.max_splits - 1) ? L : min(t0 + S, L);
   attend_segment<1>(p, vt, qs, vt, 0, r, g, t0, t1, nsplit == 1, (int64_t)split * p.batch + r,
-                    p.k_store && t1 == L ? L - 1 : -1);
+                    p.k_store && t1 == L ? L - 1 : -1, p.req_rows ? p.req_rows[r] : r);
 }
 
 // Balanced ranges: workgroup b of G owns flattened keys [b*T/G, (b+1)*T/G).
@@ -506,13 +507,15 @@ decode_balanced_kernel(DecodeParams p) {
   const bool writer = (w == 0 && blockIdx.y == 0 && lane == 0);
   int r_prev = -1;
   while (true) {
-    int r = -1;
+    int r = -1, row = 0;
     int64_t r0 = 0, r1 = 0;
     int64_t running = 0;
     for (int base = 0; base < B; base += 64) {
       if (running > end || (running == end && !last)) break;
       const int i = base + lane;
       const int Li = i < B ? max(p.seq_lens[i], 0) : 0;
+      // (the table rows come with the lengths, one round trip for both)
+      const int Ri = (i < B && p.req_rows) ? p.req_rows[i] : i;
       const int Ci = Li > 0 ? Li + kSegmentCost : 0;
       const int incl = wave_incl_scan(Ci);
       const int64_t c0 = running + (incl - Ci);
@@ -527,6 +530,7 @@ decode_balanced_kernel(DecodeParams p) {
         r = base + bit;
         r1 = running + __builtin_amdgcn_readlane(incl, bit);
         const int Lr = __builtin_amdgcn_readlane(Li, bit);
+        row = __builtin_amdgcn_readlane(Ri, bit);
         r0 = r1 - Lr;            // position of the request's first key (after its start-up)
         break;
       }
@@ -549,7 +553,7 @@ decode_balanced_kernel(DecodeParams p) {
     const int s1 = (int)(min(end, r1) - r0);
     const bool whole = r0 >= start && r1 <= end;
     attend_segment<NPAR>(p, vt, qs, pvt, par, r, g, s0, s1, whole, (int64_t)b + r,
-                         p.k_store && r1 <= end ? (int)(r1 - r0) - 1 : -1);
+                         p.k_store && r1 <= end ? (int)(r1 - r0) - 1 : -1, row);
     if (writer) {
       // workgroups holding the first and the last key of request r
       const int64_t bf = ((r0 + 1) * G - 1) / T;
