@@ -1,12 +1,12 @@
 """GPU tests of msgl_store_kv_paged_decode (store_kv of each request's new row
 and the decode in one launch).
 
-With out_loc[r] = page_table[row_r, seq_lens[r] - 1], the one launch must
-leave the pool and the outputs bit-identical to msgl_store_kv followed by
-msgl_paged_decode on the same inputs (the attention reads the newest key from
-the new row instead of the slot being written).  Both paths run on separate
-copies of the same seeded input; the fused results are also held to the
-oracle's tolerance.
+With out_loc[r] = page_table[row_r, seq_lens[r] - 1] a freshly allocated
+slot, the one launch must leave the pool and the outputs bit-identical to
+msgl_store_kv followed by msgl_paged_decode on the same inputs (the wave that
+reads a request's newest key stores it first and reads it back once its own
+store has completed).  Both paths run on separate copies of the same seeded
+input; the fused results are also held to the oracle's tolerance.
 """
 
 import sys
@@ -86,14 +86,20 @@ def test_fused_equals_store_then_decode(case):
     assert_lse_close(b[2], rl, f"fused case {case}")
 
 
-@pytest.mark.parametrize("lens_kind", ["many", "empty"])
+@pytest.mark.parametrize("lens_kind", ["many", "tiny", "straddle", "empty"])
 def test_fused_more_rows_than_workgroups_and_empty_requests(lens_kind):
     """300 requests (more new rows than resident workgroups: a workgroup
-    stores several) or empty requests (their row is still stored)."""
+    stores several); 1-4 keys each (the newest key is often a segment's only
+    key); lengths of 33-95 keys (the newest key in the first or the second
+    wave's tile); or empty requests (their row is still stored)."""
     banner(f"fused {lens_kind}")
     rng = np.random.default_rng(11)
     if lens_kind == "many":
         lens = rng.integers(1, 400, 300)
+    elif lens_kind == "tiny":
+        lens = rng.integers(1, 5, 300)
+    elif lens_kind == "straddle":
+        lens = rng.integers(33, 96, 200)
     else:
         lens = rng.integers(1, 900, 40)
     inp = small_decode(98, 32, 8, lens, num_slots=1 << 18)
