@@ -86,8 +86,9 @@ struct DecodeParams {
   int32_t* meta;          // balanced mode: per request (first, last) workgroup
   // Store fused into the launch (k_store null: none).  Row r of k_new /
   // v_new is request r's newest token, stored at slot out_loc[r], which is
-  // key seq_lens[r] - 1 of the request; the attention takes that key from
-  // the new row itself, so no workgroup reads a slot another one writes.
+  // key seq_lens[r] - 1 of the request; the one wave per kv head that reads
+  // that key stores it first (see attend_segment), so no workgroup reads a
+  // slot another one writes.
   char* k_store;
   char* v_store;
   const char* k_new;
@@ -95,7 +96,6 @@ struct DecodeParams {
   int64_t new_stride_bytes;
   const void* out_loc;
   int32_t out_loc_i64;
-  int32_t row_units;      // 16-byte units of one K (or V) row
 };
 
 // The lane index, hidden from loop-invariant code motion: per-lane addresses
@@ -651,7 +651,6 @@ hipError_t launch_paged_decode(const DecodeArgs& a) {
   p.new_stride_bytes = a.new_stride * 2;
   p.out_loc = a.out_loc;
   p.out_loc_i64 = a.out_loc_is_i64 ? 1 : 0;
-  p.row_units = a.num_kv_heads * kHeadDim * 2 / 16;
 
   hipError_t err;
   switch (decode_kv_heads_per_block(a.num_kv_heads)) {
