@@ -319,6 +319,48 @@ int msgl_merge_states(void* out, float* lse_out, const float* part_out,
                       hipStream_t stream);
 
 /*
+ * Validation alone.  msgl_validate_<call> takes the arguments of msgl_<call>
+ * without the stream, runs the same host-side checks in the same order and
+ * returns the status that call would return before its first HIP call:
+ * MSGL_OK where the call would enqueue its kernels, else the error code, with
+ * msgl_last_error() describing it.  It makes no HIP call, so it works on a
+ * host without a GPU; pointers are checked for NULL and alignment only, never
+ * dereferenced.
+ */
+int msgl_validate_store_kv(void* k_cache, void* v_cache, int64_t num_slots,
+                           int64_t cache_row_stride, const void* k_new, const void* v_new,
+                           int64_t new_row_stride, const void* out_loc, int32_t index_dtype,
+                           int64_t n, int32_t num_kv_heads, int32_t head_dim, int32_t dtype);
+int msgl_validate_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_stride,
+                               const void* k_cache, const void* v_cache, int64_t num_slots,
+                               int64_t cache_row_stride, const int32_t* page_table,
+                               int64_t page_table_stride, const int32_t* req_rows,
+                               const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                               int32_t max_seq_len, float sm_scale, int32_t split_tokens,
+                               void* workspace, size_t workspace_bytes);
+int msgl_validate_store_kv_paged_decode(
+    void* out, float* lse_out, const void* q, int64_t q_row_stride, void* k_cache, void* v_cache,
+    int64_t num_slots, int64_t cache_row_stride, const void* k_new, const void* v_new,
+    int64_t new_row_stride, const void* out_loc, int32_t index_dtype, const int32_t* page_table,
+    int64_t page_table_stride, const int32_t* req_rows, const int32_t* seq_lens, int32_t batch,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    int32_t max_seq_len, float sm_scale, int32_t split_tokens, void* workspace,
+    size_t workspace_bytes);
+int msgl_validate_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_stride,
+                               const void* k_cache, const void* v_cache, int64_t num_slots,
+                               int64_t cache_row_stride, const int32_t* page_table,
+                               int64_t page_table_stride, const int32_t* req_rows,
+                               const int32_t* prefix_lens, const int32_t* extend_lens,
+                               const int32_t* q_offsets, int32_t batch, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                               int32_t max_extend_len, int32_t max_kv_len, float sm_scale,
+                               int32_t causal, void* workspace, size_t workspace_bytes);
+int msgl_validate_merge_states(void* out, float* lse_out, const float* part_out,
+                               const float* part_lse, int32_t num_parts, int64_t n,
+                               int32_t num_heads, int32_t head_dim, int32_t out_dtype);
+
+/*
  * Graph-replayed decode step ["Mini-SGLang complete analysis" §4.6.6 (the
  * attention backend's persistent capture buffers, live data written in place
  * before replay), §5.3 (one graph per batch size of [1, 2, 4, 8, 16, 24, ...,

@@ -61,6 +61,25 @@ SIGNATURES = {
                                        _c_void_p, _i64, _c_void_p, _c_void_p, _f32, _c_void_p,
                                        _c_void_p, _i64, _c_void_p, _i32, _i64, _i32, _i32, _i32,
                                        _c_void_p]),
+    "msgl_validate_store_kv": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p,
+                                      _i64, _c_void_p, _i32, _i64, _i32, _i32, _i32]),
+    "msgl_validate_paged_decode": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
+                                          _c_void_p, _i64, _i64, _c_void_p, _i64, _c_void_p,
+                                          _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                          _i32, _c_void_p, _size_t]),
+    "msgl_validate_store_kv_paged_decode": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64,
+                                                   _c_void_p, _c_void_p, _i64, _i64, _c_void_p,
+                                                   _c_void_p, _i64, _c_void_p, _i32, _c_void_p,
+                                                   _i64, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                                   _i32, _i32, _i32, _f32, _i32, _c_void_p,
+                                                   _size_t]),
+    "msgl_validate_paged_extend": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
+                                          _c_void_p, _i64, _i64, _c_void_p, _i64, _c_void_p,
+                                          _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                          _i32, _i32, _i32, _i32, _f32, _i32, _c_void_p,
+                                          _size_t]),
+    "msgl_validate_merge_states": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
+                                          _i64, _i32, _i32, _i32]),
     "msgl_decode_graph_layout": (_i32, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_size_t)]),
     "msgl_decode_graph_create": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _i64, _i32,
                                         _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,

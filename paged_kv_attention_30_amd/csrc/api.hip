@@ -17,6 +17,18 @@
 namespace {
 
 thread_local char g_last_error[512] = "";
+// Set by the msgl_validate_* calls: the entry point returns MSGL_OK where it
+// would make its first HIP call.
+thread_local bool g_validate_only = false;
+
+// Runs `call` (an entry point invocation) with launches suppressed.
+template <typename F>
+int validate_only(F call) {
+  g_validate_only = true;
+  const int st = call();
+  g_validate_only = false;
+  return st;
+}
 
 int fail(int status, const char* file, int line, const char* fmt, ...) {
   char msg[400];
@@ -176,6 +188,7 @@ int msgl_store_kv(void* k_cache, void* v_cache, int64_t num_slots, int64_t cache
     unit /= 2;
   }
   a.unit_bytes = unit;
+  if (g_validate_only) return MSGL_OK;
   return launch_status(msgl::launch_store_kv(a), "store_kv");
 }
 
@@ -285,6 +298,7 @@ int paged_decode_impl(void* out, float* lse_out, const void* q, int64_t q_row_st
   a.part_lse = need ? (float*)((char*)workspace + ws.part_out_bytes) : nullptr;
   a.meta = ws.meta_bytes ? (int32_t*)((char*)workspace + ws.part_out_bytes + ws.part_lse_bytes)
                          : nullptr;
+  if (g_validate_only) return MSGL_OK;
   if (split_tokens > 0) {
     a.balanced_blocks = 0;
     a.max_splits = need ? (int32_t)(((int64_t)max_seq_len + split_tokens - 1) / split_tokens) : 1;
@@ -408,6 +422,7 @@ int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_st
   a.workspace = workspace;
   a.workspace_bytes = workspace_bytes;
   a.stream = stream;
+  if (g_validate_only) return MSGL_OK;
   return launch_status(msgl::launch_paged_extend(a), "paged_extend");
 }
 
@@ -564,7 +579,80 @@ int msgl_merge_states(void* out, float* lse_out, const float* part_out, const fl
   a.split_tokens = 0;
   a.meta = nullptr;
   a.stream = stream;
+  if (g_validate_only) return MSGL_OK;
   return launch_status(msgl::launch_merge(a), "merge_states");
+}
+
+int msgl_validate_store_kv(void* k_cache, void* v_cache, int64_t num_slots,
+                           int64_t cache_row_stride, const void* k_new, const void* v_new,
+                           int64_t new_row_stride, const void* out_loc, int32_t index_dtype,
+                           int64_t n, int32_t num_kv_heads, int32_t head_dim, int32_t dtype) {
+  return validate_only([&] {
+    return msgl_store_kv(k_cache, v_cache, num_slots, cache_row_stride, k_new, v_new,
+                         new_row_stride, out_loc, index_dtype, n, num_kv_heads, head_dim, dtype,
+                         nullptr);
+  });
+}
+
+int msgl_validate_paged_decode(void* out, float* lse_out, const void* q, int64_t q_row_stride,
+                               const void* k_cache, const void* v_cache, int64_t num_slots,
+                               int64_t cache_row_stride, const int32_t* page_table,
+                               int64_t page_table_stride, const int32_t* req_rows,
+                               const int32_t* seq_lens, int32_t batch, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                               int32_t max_seq_len, float sm_scale, int32_t split_tokens,
+                               void* workspace, size_t workspace_bytes) {
+  return validate_only([&] {
+    return msgl_paged_decode(out, lse_out, q, q_row_stride, k_cache, v_cache, num_slots,
+                             cache_row_stride, page_table, page_table_stride, req_rows, seq_lens,
+                             batch, num_q_heads, num_kv_heads, head_dim, page_size, max_seq_len,
+                             sm_scale, split_tokens, workspace, workspace_bytes, nullptr);
+  });
+}
+
+int msgl_validate_store_kv_paged_decode(
+    void* out, float* lse_out, const void* q, int64_t q_row_stride, void* k_cache, void* v_cache,
+    int64_t num_slots, int64_t cache_row_stride, const void* k_new, const void* v_new,
+    int64_t new_row_stride, const void* out_loc, int32_t index_dtype, const int32_t* page_table,
+    int64_t page_table_stride, const int32_t* req_rows, const int32_t* seq_lens, int32_t batch,
+    int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+    int32_t max_seq_len, float sm_scale, int32_t split_tokens, void* workspace,
+    size_t workspace_bytes) {
+  return validate_only([&] {
+    return msgl_store_kv_paged_decode(out, lse_out, q, q_row_stride, k_cache, v_cache, num_slots,
+                                      cache_row_stride, k_new, v_new, new_row_stride, out_loc,
+                                      index_dtype, page_table, page_table_stride, req_rows,
+                                      seq_lens, batch, num_q_heads, num_kv_heads, head_dim,
+                                      page_size, max_seq_len, sm_scale, split_tokens, workspace,
+                                      workspace_bytes, nullptr);
+  });
+}
+
+int msgl_validate_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_stride,
+                               const void* k_cache, const void* v_cache, int64_t num_slots,
+                               int64_t cache_row_stride, const int32_t* page_table,
+                               int64_t page_table_stride, const int32_t* req_rows,
+                               const int32_t* prefix_lens, const int32_t* extend_lens,
+                               const int32_t* q_offsets, int32_t batch, int32_t num_q_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                               int32_t max_extend_len, int32_t max_kv_len, float sm_scale,
+                               int32_t causal, void* workspace, size_t workspace_bytes) {
+  return validate_only([&] {
+    return msgl_paged_extend(out, lse_out, q, q_row_stride, k_cache, v_cache, num_slots,
+                             cache_row_stride, page_table, page_table_stride, req_rows,
+                             prefix_lens, extend_lens, q_offsets, batch, num_q_heads,
+                             num_kv_heads, head_dim, page_size, max_extend_len, max_kv_len,
+                             sm_scale, causal, workspace, workspace_bytes, nullptr);
+  });
+}
+
+int msgl_validate_merge_states(void* out, float* lse_out, const float* part_out,
+                               const float* part_lse, int32_t num_parts, int64_t n,
+                               int32_t num_heads, int32_t head_dim, int32_t out_dtype) {
+  return validate_only([&] {
+    return msgl_merge_states(out, lse_out, part_out, part_lse, num_parts, n, num_heads, head_dim,
+                             out_dtype, nullptr);
+  });
 }
 
 }  // extern "C"

@@ -319,3 +319,96 @@ def test_prologue_validation(lib):
     assert pro(qkvs=48 * 128 + 4) == ALIGN
     assert pro(cs=8 * 128 + 4) == ALIGN          # pool rows must stay 16-byte aligned
     assert pro(k=FAKE + 8) == ALIGN
+
+
+# ---------------------------------------------------------------------------
+# msgl_validate_*: the same checks with no HIP call, so valid arguments can be
+# checked on a host without a GPU (every call below would otherwise launch)
+# ---------------------------------------------------------------------------
+
+def _validate_decode(lib, fused_call=False, **kw):
+    a = dict(out=FAKE, lse=FAKE, q=FAKE, q_stride=32 * 128, k=FAKE, v=FAKE2, slots=1024,
+             cstride=8 * 128, knew=FAKE, vnew=FAKE2, nstride=8 * 128, loc=FAKE, idx=0,
+             pt=FAKE, pt_stride=4096, rows=None, lens=FAKE, batch=4, hq=32, hkv=8, d=128,
+             page=1, max_len=4096, scale=0.088, split=0, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    if fused_call:
+        return lib.msgl_validate_store_kv_paged_decode(
+            a["out"], a["lse"], a["q"], a["q_stride"], a["k"], a["v"], a["slots"], a["cstride"],
+            a["knew"], a["vnew"], a["nstride"], a["loc"], a["idx"], a["pt"], a["pt_stride"],
+            a["rows"], a["lens"], a["batch"], a["hq"], a["hkv"], a["d"], a["page"],
+            a["max_len"], a["scale"], a["split"], a["ws"], a["ws_bytes"])
+    return lib.msgl_validate_paged_decode(
+        a["out"], a["lse"], a["q"], a["q_stride"], a["k"], a["v"], a["slots"], a["cstride"],
+        a["pt"], a["pt_stride"], a["rows"], a["lens"], a["batch"], a["hq"], a["hkv"], a["d"],
+        a["page"], a["max_len"], a["scale"], a["split"], a["ws"], a["ws_bytes"])
+
+
+@pytest.mark.parametrize("fused_call", [False, True])
+def test_validate_decode_accepts_valid_arguments(lib, fused_call):
+    assert _validate_decode(lib, fused_call) == OK, lib.msgl_last_error()
+    assert lib.msgl_last_error() == b""
+    # fixed chunks, a GQA ratio of 8, page_size 16, identity rows left out, no lse
+    assert _validate_decode(lib, fused_call, split=256, hq=64, q_stride=64 * 128, page=16,
+                            lse=None) == OK
+    # fixed chunks with one chunk per request need no workspace
+    assert _validate_decode(lib, fused_call, split=4096, ws=None, ws_bytes=0) == OK
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(k=None), NULL), (dict(d=64), UNSUP), (dict(cstride=100), SHAPE),
+    (dict(q=FAKE + 4), ALIGN), (dict(ws=None, ws_bytes=0), WS), (dict(split=48), SHAPE),
+])
+def test_validate_decode_returns_the_call_status(lib, kw, code):
+    assert _validate_decode(lib, **kw) == code
+    assert decode(lib, **kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(knew=None), NULL), (dict(idx=7), UNSUP), (dict(nstride=100), SHAPE),
+    (dict(knew=FAKE + 8), ALIGN),
+])
+def test_validate_store_decode_returns_the_call_status(lib, kw, code):
+    assert _validate_decode(lib, True, **kw) == code
+    assert fused(lib, **kw) == code
+
+
+def test_validate_store_kv(lib):
+    def v(**kw):
+        a = dict(k=FAKE, v=FAKE2, slots=1024, cstride=8 * 128, knew=FAKE, vnew=FAKE2,
+                 nstride=8 * 128, loc=FAKE, idx=1, n=64, hkv=8, d=128, dtype=0)
+        a.update(kw)
+        return lib.msgl_validate_store_kv(a["k"], a["v"], a["slots"], a["cstride"], a["knew"],
+                                          a["vnew"], a["nstride"], a["loc"], a["idx"], a["n"],
+                                          a["hkv"], a["d"], a["dtype"])
+    assert v() == OK and v(dtype=1, idx=0) == OK and v(n=0, loc=None) == OK
+    assert v(loc=None) == NULL and v(idx=3) == UNSUP and v(nstride=100) == SHAPE
+    assert v(n=-1) == SHAPE and v(dtype=5) == UNSUP
+
+
+def test_validate_extend(lib):
+    def v(**kw):
+        a = dict(out=FAKE, lse=FAKE, q=FAKE, q_stride=32 * 128, k=FAKE, v=FAKE2, slots=1024,
+                 cstride=8 * 128, pt=FAKE, pt_stride=4096, rows=None, pre=FAKE, ext=FAKE,
+                 off=FAKE, batch=2, hq=32, hkv=8, d=128, page=1, max_ext=512, max_kv=4096,
+                 scale=0.088, causal=1, ws=FAKE, ws_bytes=1 << 20)
+        a.update(kw)
+        return lib.msgl_validate_paged_extend(
+            a["out"], a["lse"], a["q"], a["q_stride"], a["k"], a["v"], a["slots"], a["cstride"],
+            a["pt"], a["pt_stride"], a["rows"], a["pre"], a["ext"], a["off"], a["batch"],
+            a["hq"], a["hkv"], a["d"], a["page"], a["max_ext"], a["max_kv"], a["scale"],
+            a["causal"], a["ws"], a["ws_bytes"])
+    assert v() == OK and v(ws=None, ws_bytes=0) == OK and v(hq=8, page=16) == OK
+    assert v(causal=0) == UNSUP and v(pre=None) == NULL and v(ws_bytes=8) == WS
+    assert v(max_kv=100) == SHAPE
+
+
+def test_validate_merge_states(lib):
+    def v(**kw):
+        a = dict(out=FAKE, lse=FAKE, po=FAKE, pl=FAKE2, parts=4, n=64, heads=32, d=128, dt=0)
+        a.update(kw)
+        return lib.msgl_validate_merge_states(a["out"], a["lse"], a["po"], a["pl"], a["parts"],
+                                              a["n"], a["heads"], a["d"], a["dt"])
+    assert v() == OK and v(dt=1, lse=None) == OK and v(n=0, out=None) == OK
+    assert v(parts=0) == SHAPE and v(po=None) == NULL and v(d=6) == UNSUP
+    assert v(po=FAKE + 4) == ALIGN
