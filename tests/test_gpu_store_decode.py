@@ -115,6 +115,36 @@ def test_fused_more_rows_than_workgroups_and_empty_requests(lens_kind):
         assert np.all(out[[0, 17, 39]] == 0)
 
 
+def test_fused_one_chunk_per_request_and_identity_rows():
+    """Fixed chunks wider than every request (one chunk each, no workspace)
+    and no req_rows (request r reads table row r)."""
+    banner("fused one chunk, identity rows")
+    inp = small_decode(120, 32, 8, [700, 1, 129, 33], num_slots=4096)
+    # the identity mapping needs the table rows in request order
+    inp.page_table = np.ascontiguousarray(inp.page_table[inp.dec_req_rows])
+    inp.dec_req_rows = np.arange(inp.num_decode, dtype=np.int32)
+    d_lens = up(inp.dec_seq_lens)
+    runs = []
+    for fused_call in (False, True):
+        u = Uploaded(inp)
+        loc = up(inp.out_loc.astype(np.int32))
+        if fused_call:
+            out, lse = msgl.store_kv_paged_decode(u.dq, u.k, u.v, u.k_new, u.v_new, loc, u.pt,
+                                                  d_lens, u.d_max, inp.sm_scale,
+                                                  split_tokens=1024)
+        else:
+            msgl.store_kv(u.k, u.v, u.k_new, u.v_new, loc)
+            out, lse = msgl.paged_decode(u.dq, u.k, u.v, u.pt, d_lens, u.d_max, inp.sm_scale,
+                                         split_tokens=1024)
+        runs.append((u, out, lse))
+    assert_same(runs[0], runs[1], "one chunk")
+    kp, vp = oracle.store_kv(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.out_loc)
+    ro, rl = oracle.paged_decode(inp.dec_q, kp, vp, inp.page_table, inp.dec_req_rows,
+                                 inp.dec_seq_lens, inp.sm_scale, inp.num_kv_heads)
+    assert_close(runs[1][1], ro, "fused one chunk")
+    assert_lse_close(runs[1][2], rl, "fused one chunk")
+
+
 def test_fused_full_c2_in_the_bench_launch():
     """The 64-request, 512K-slot decode batch as the benchmark times it."""
     banner("fused C2 full size")
