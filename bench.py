@@ -309,6 +309,33 @@ def load_traffic(khash: str):
         return None
 
 
+def host_description() -> str:
+    """CPU model, logical CPUs visible / usable, and the BLAS numpy uses."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        usable = os.cpu_count()
+    blas = "unknown BLAS"
+    try:
+        from threadpoolctl import threadpool_info
+        libs = [f"{d.get('internal_api')} ({d.get('num_threads')} threads)"
+                for d in threadpool_info() if d.get("user_api") == "blas"]
+        if libs:
+            blas = ", ".join(libs)
+    except ImportError:  # pragma: no cover
+        pass
+    return f"{model}, {os.cpu_count()} logical CPUs visible, {usable} usable; numpy BLAS {blas}"
+
+
 def cpu_baseline(inp, budget_s: float = 12.0):
     """Time the oracle on a bounded sample of the decode workload (rank 0):
     passes over the batch's requests, one request at a time, until about
@@ -334,6 +361,7 @@ def cpu_baseline(inp, budget_s: float = 12.0):
                                                 inp.dec_seq_lens[sel], inp.num_kv_heads, 128)
             done += 1
         dt = time.perf_counter() - t0
+        host = host_description()      # (inside the 1-thread limit)
     finally:
         if ctx is not None:
             ctx.__exit__(None, None, None)
@@ -341,8 +369,7 @@ def cpu_baseline(inp, budget_s: float = 12.0):
             "sample": f"fp64 numpy oracle decode, one request at a time, {done} request-decodes "
                       f"({done / inp.num_decode:.1f} passes over the {inp.num_decode}-request headline "
                       f"batch, {kv_bytes / 1e6:.1f} MB of K/V) in {dt:.1f} s, "
-                      f"BLAS limited to 1 thread; host {platform.processor() or platform.machine()}, "
-                      f"{os.cpu_count()} logical CPUs visible"}
+                      f"BLAS limited to 1 thread; host {host}"}
 
 
 def embedding_run(steps: int, warmup: int):
