@@ -327,7 +327,8 @@ def host_description() -> str:
     blas = "unknown BLAS"
     try:
         from threadpoolctl import threadpool_info
-        libs = [f"{d.get('internal_api')} ({d.get('num_threads')} threads)"
+        libs = [f"{d.get('internal_api')} ({d.get('num_threads')} "
+                f"thread{'' if d.get('num_threads') == 1 else 's'})"
                 for d in threadpool_info() if d.get("user_api") == "blas"]
         if libs:
             blas = ", ".join(libs)
