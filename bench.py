@@ -35,10 +35,16 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "paged decode KV GB/s + extend TFLOP/s on 1 MI355X, % of roofline"
-KERNEL_SOURCES = ["decode.hip", "merge.hip", "common.hpp"]
+# every library source and the public headers: a stored traffic figure is
+# used only while none of them has changed since the counters were taken
+CSRC_DIR = os.path.join(ROOT, "paged_kv_attention_30_amd", "csrc")
+INCLUDE_DIR = os.path.join(ROOT, "include")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_c2_traffic.md")
 
 WORKLOAD_TEXT = {
+    "C1": "tiny paged GQA decode + store_kv: Hq 16 / Hkv 8 / D 128, batch 4, kv lens "
+          "[17, 64, 100, 255], 1,024-slot randomly permuted pool, page_size 1, bf16 N(0,1), "
+          "seed 1 (latency-bound: 1.8 MB of K/V)",
     "C2": "paged GQA decode + store_kv: Hq 32 / Hkv 8 / D 128, batch 64, kv lens U[512,4096], "
           "524,288-slot randomly permuted pool, page_size 1, bf16 N(0,1), seed 2",
     "C3": "causal chunked-prefill extend + store_kv: Hq 32 / Hkv 8 / D 128, batch 8, prefixes "
@@ -69,10 +75,18 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+def kernel_sources() -> list:
+    files = [os.path.join(CSRC_DIR, f) for f in os.listdir(CSRC_DIR)]
+    files += [os.path.join(INCLUDE_DIR, f) for f in os.listdir(INCLUDE_DIR)]
+    return sorted(f for f in files if f.endswith((".hip", ".hpp", ".cpp", ".h")))
+
+
 def kernel_hash() -> str:
+    """Hash of every library source file (names and contents)."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_kv_attention_30_amd", "csrc", f), "rb") as fh:
+    for f in kernel_sources():
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
@@ -337,40 +351,123 @@ def host_description() -> str:
     return f"{model}, {os.cpu_count()} logical CPUs visible, {usable} usable; numpy BLAS {blas}"
 
 
-def cpu_baseline(inp, budget_s: float = 12.0):
-    """Time the oracle on a bounded sample of the decode workload (rank 0):
-    passes over the batch's requests, one request at a time, until about
-    ``budget_s`` seconds of CPU work are done."""
+# --- CPU baseline: the oracle on the host cores ------------------------------
+# The oracle's page-table walk is a Python loop (it holds the interpreter lock),
+# so "all cores" means a pool of forked worker processes, each with one BLAS
+# thread; it runs before the GPU is initialised, so forking is safe.  The
+# workload being timed sits in this module global when the pool forks, and
+# the workers read it copy-on-write.
+_CPU_JOB = {}
+
+
+def _cpu_task(task):
     import oracle
-    from workloads import metrics
-    try:
-        from threadpoolctl import threadpool_limits
-    except ImportError:  # pragma: no cover
-        threadpool_limits = None
-    ctx = threadpool_limits(limits=1) if threadpool_limits else None
-    try:
+    kind, a, b = task
+    j = _CPU_JOB
+    if kind == "decode":
+        inp = j["inp"]
+        sel = slice(a, b)
+        oracle.paged_decode(inp.dec_q[sel], j["kp"], j["vp"], inp.page_table,
+                            inp.dec_req_rows[sel], inp.dec_seq_lens[sel], inp.sm_scale,
+                            inp.num_kv_heads)
+    else:
+        inp = j["inp"]
+        oracle.paged_extend(inp.ext_q, j["kp"], j["vp"], inp.page_table, inp.ext_req_rows,
+                            inp.ext_prefix_lens, inp.ext_extend_lens, inp.ext_q_offsets,
+                            inp.sm_scale, inp.num_kv_heads, query_subset=j["rows"][a:b])
+    return 0
+
+
+def _time_tasks(tasks, workers: int, reps: int = 3) -> float:
+    """Median wall time of ``reps`` passes over ``tasks`` after one warm-up
+    pass: in this process (``workers`` = 1) or spread over a forked pool."""
+    import multiprocessing as mp
+    from threadpoolctl import threadpool_limits
+    times = []
+    with threadpool_limits(limits=1):
+        if workers == 1:
+            for i in range(reps + 1):
+                t0 = time.perf_counter()
+                for t in tasks:
+                    _cpu_task(t)
+                if i:
+                    times.append(time.perf_counter() - t0)
+        else:
+            with mp.get_context("fork").Pool(workers) as pool:
+                for i in range(reps + 1):
+                    t0 = time.perf_counter()
+                    pool.map(_cpu_task, tasks, chunksize=1)
+                    if i:
+                        times.append(time.perf_counter() - t0)
+    return float(np.median(times))
+
+
+def cpu_baselines() -> dict:
+    """The fp64 oracle timed on the host (rank 0, before the GPU is touched):
+    on one core and on every usable core, median of 3 passes after 1 warm-up.
+
+    Decode: the whole tiny batch, the whole headline batch and the first 32
+    decode requests of the mixed batch (GB/s of distinct K/V read).  Extend:
+    8 query rows spread over each request of the chunked-prefill batch
+    (TFLOP/s of causal pairs).  Per-request (decode) or 4-row (extend) tasks;
+    both modes run the same task list."""
+    import oracle
+    from workloads import make_config, metrics
+    usable = len(os.sched_getaffinity(0))
+    workers = max(1, min(usable, 16))
+    host = host_description()
+    res = {}
+
+    def decode_case(name, nreq):
+        inp = make_config(name)
         kp, vp = oracle.store_kv(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.out_loc)
-        done = 0
-        t0 = time.perf_counter()
-        kv_bytes = 0
-        while time.perf_counter() - t0 < budget_s:
-            i = done % inp.num_decode
-            sel = slice(i, i + 1)
-            oracle.paged_decode(inp.dec_q[sel], kp, vp, inp.page_table, inp.dec_req_rows[sel],
-                                inp.dec_seq_lens[sel], inp.sm_scale, inp.num_kv_heads)
-            kv_bytes += metrics.decode_kv_bytes(inp.page_table, inp.dec_req_rows[sel],
-                                                inp.dec_seq_lens[sel], inp.num_kv_heads, 128)
-            done += 1
-        dt = time.perf_counter() - t0
-        host = host_description()      # (inside the 1-thread limit)
-    finally:
-        if ctx is not None:
-            ctx.__exit__(None, None, None)
-    return {"value": round(kv_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"fp64 numpy oracle decode, one request at a time, {done} request-decodes "
-                      f"({done / inp.num_decode:.1f} passes over the {inp.num_decode}-request headline "
-                      f"batch, {kv_bytes / 1e6:.1f} MB of K/V) in {dt:.1f} s, "
-                      f"BLAS limited to 1 thread; host {host}"}
+        n = min(nreq, inp.num_decode)
+        _CPU_JOB.clear()
+        _CPU_JOB.update(inp=inp, kp=kp, vp=vp)
+        kv = metrics.decode_kv_bytes(inp.page_table, inp.dec_req_rows[:n], inp.dec_seq_lens[:n],
+                                     inp.num_kv_heads, 128)
+        tasks = [("decode", i, i + 1) for i in range(n)]
+        t1 = _time_tasks(tasks, 1)
+        tn = _time_tasks(tasks, workers)
+        _CPU_JOB.clear()
+        return {"requests": n, "kv_mb": round(kv / 1e6, 2),
+                "one_core_s": round(t1, 4), "one_core_GBps": round(kv / t1 / 1e9, 4),
+                "all_cores_s": round(tn, 4), "all_cores_GBps": round(kv / tn / 1e9, 4),
+                "requests_per_s_all_cores": round(n / tn, 2)}
+
+    log("CPU baseline: decode C1 / C2 / C5a")
+    res["C1"] = decode_case("C1", 4)
+    res["C2"] = decode_case("C2", 64)
+    res["C5a_decode"] = decode_case("C5a", 32)
+
+    log("CPU baseline: extend C3")
+    inp = make_config("C3")
+    kp, vp = oracle.store_kv(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.out_loc)
+    rows, pairs = [], 0
+    for r in range(inp.num_extend):
+        base, E, P = int(inp.ext_q_offsets[r]), int(inp.ext_extend_lens[r]), int(inp.ext_prefix_lens[r])
+        for i in np.linspace(0, E - 1, 8).astype(int).tolist():
+            rows.append(base + i)
+            pairs += P + i + 1
+    _CPU_JOB.clear()
+    _CPU_JOB.update(inp=inp, kp=kp, vp=vp, rows=rows)
+    tasks = [("extend", a, a + 4) for a in range(0, len(rows), 4)]
+    flops = 4 * inp.num_q_heads * 128 * pairs
+    t1 = _time_tasks(tasks, 1)
+    tn = _time_tasks(tasks, workers)
+    _CPU_JOB.clear()
+    res["C3_extend"] = {"query_rows": len(rows), "causal_pairs": pairs, "flops": flops,
+                        "one_core_s": round(t1, 4), "one_core_TFLOPs": round(flops / t1 / 1e12, 6),
+                        "all_cores_s": round(tn, 4), "all_cores_TFLOPs": round(flops / tn / 1e12, 6)}
+    c2 = res["C2"]
+    return {"value": c2["all_cores_GBps"], "unit": "GB/s", "cores": workers, "kind": "oracle",
+            "sample": (f"fp64 numpy oracle, whole 64-request headline decode batch "
+                       f"({c2['kv_mb']} MB of distinct K/V), one process per request over "
+                       f"{workers} worker processes with 1 BLAS thread each, median of 3 passes "
+                       f"after 1 warm-up; per-workload one-core and all-core figures (decode "
+                       f"C1, C2, C5a, extend C3) under 'workloads'"),
+            "one_core": {"value": c2["one_core_GBps"], "unit": "GB/s", "cores": 1},
+            "workloads": res, "host": host}
 
 
 def embedding_run(steps: int, warmup: int):
@@ -560,7 +657,7 @@ def decode_figures(inp, res, steps, fused=False):
     kv = metrics.decode_kv_bytes(inp.page_table, inp.dec_req_rows, inp.dec_seq_lens,
                                  inp.num_kv_heads, 128)
     alg = metrics.decode_bytes(inp.page_table, inp.dec_req_rows, inp.dec_seq_lens,
-                               inp.num_q_heads, inp.num_kv_heads, 128)
+                               inp.num_q_heads, inp.num_kv_heads, 128, page_size=inp.page_size)
     if fused:
         alg += store_bytes_of(inp)
     dec_ms = float(np.mean(res["dec_ms"]))
@@ -612,8 +709,8 @@ def main(argv=None) -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--configs", default="C3,C4,C5a,C5b,EMB,PRO",
-                    help="extra workloads (comma list of C3,C4,C5a,C5b,EMB,PRO; '' for none)")
+    ap.add_argument("--configs", default="C1,C3,C4,C5a,C5b,EMB,PRO",
+                    help="extra workloads (comma list of C1,C3,C4,C5a,C5b,EMB,PRO; '' for none)")
     ap.add_argument("--split-tokens", type=int, default=0)
     ap.add_argument("--separate-store", action="store_true",
                     help="decode-only batches: store_kv and the decode as two launches")
@@ -632,6 +729,11 @@ def main(argv=None) -> int:
               "shards by request or by kv head with no exchange between GPUs)",
               file=sys.stderr)
         return 2
+
+    cpu = None
+    if not args.no_cpu_baseline and not args.only:
+        # before anything initialises the GPU: the pool forks this process
+        cpu = cpu_baselines()
 
     import torch
     import paged_kv_attention_30_amd as msgl
@@ -712,11 +814,6 @@ def main(argv=None) -> int:
         extras[name] = summarize(name, inp_x, run_x, res_x, max(5, args.steps // 5))
         del run_x
         torch.cuda.empty_cache()
-
-    cpu = None
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a bounded sample")
-        cpu = cpu_baseline(inp)
 
     line = {
         "metric": METRIC,

@@ -281,6 +281,7 @@ int paged_decode_impl(void* out, float* lse_out, const void* q, int64_t q_row_st
   a.q_stride = q_row_stride;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
+  a.num_slots = num_slots;
   a.cache_stride = cache_row_stride;
   a.page_table = page_table;
   a.pt_stride = page_table_stride;

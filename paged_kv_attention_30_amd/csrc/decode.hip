@@ -8,9 +8,15 @@
 // view), so key j of a request sits in slot page_table[row, j]; §4.6.7 — the
 // new token was stored before the kernel runs, so seq_len counts it.
 //
-// gfx950 design.  A workgroup has one wave per kv head (up to 8) and walks
-// one range of keys; all its waves read the same tokens, so every gathered
-// K/V row (num_kv_heads x 256 B) is fetched by one workgroup at one time.
+// gfx950 design.  A workgroup has two waves per kv head (up to 8 heads, 16
+// waves) and walks one range of keys; all its waves read the same tokens, so
+// every gathered K/V row (num_kv_heads x 256 B) is fetched by one workgroup
+// at one time.
+// * Page table: with page_size P > 1 (a power of two) the slots of a page
+//   are consecutive, so only the page's first column is read and key j sits
+//   in slot page_table[row, j - j % P] + j % P — the every-P-th-column view
+//   of §4.6.4; P = 1 (or any other P) reads every column.  Slots are clamped
+//   to the pool, so a bad entry cannot address memory outside it.
 // * Work split ("balanced" mode, split_tokens = 0): the keys of the whole
 //   batch, laid end to end in request order, are cut into gridDim.x equal
 //   ranges, one per workgroup; the grid is sized to the number of
@@ -75,6 +81,8 @@ struct DecodeParams {
   int64_t pt_stride;
   const int32_t* req_rows;
   const int32_t* seq_lens;
+  uint32_t slot_max;      // num_slots - 1 (slots are clamped to the pool)
+  int32_t page_mask;      // page_size - 1 for a power-of-two page_size, else 0
   int32_t batch;
   int32_t num_q_heads;
   int32_t ratio;
@@ -128,6 +136,14 @@ __device__ __forceinline__ void store_slice(const DecodeParams& p, int r, int g,
     st16((lane < 16 ? p.k_store : p.v_store) + slot * p.cache_stride_bytes +
              (int64_t)g * kHeadDim * 2 + 16 * (lane & 15),
          v);
+}
+
+// Slot of key `key` of a request whose table row starts at `pt`: read from
+// the column of the key's page start, offset inside the page, clamped to the
+// pool (negative entries clamp to the last slot).
+__device__ __forceinline__ int slot_of(const DecodeParams& p, const int32_t* pt, int key) {
+  const int off = key & p.page_mask;
+  return (int)min((uint32_t)(pt[key - off] + off), p.slot_max);
 }
 
 // A wave's V tile: key-major rows of 128 dims (256 bytes); the 8-byte group
@@ -251,8 +267,8 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
   // so each iteration waits on one memory latency (its K/V), not two.
   constexpr int kStep = kTile * NPAR;
   const int tfirst = t0 + kTile * par;
-  int na = pt[min(tfirst + c, t1 - 1)];
-  int nb = pt[min(tfirst + 16 + c, t1 - 1)];
+  int na = slot_of(p, pt, min(tfirst + c, t1 - 1));
+  int nb = slot_of(p, pt, min(tfirst + 16 + c, t1 - 1));
   __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
@@ -293,8 +309,8 @@ __device__ __forceinline__ void attend_segment(const DecodeParams& p, uint16_t* 
       kb[kk] = ld16(rb + 64 * kk);
     }
     if (tb + kStep < t1) {
-      na = pt[min(tb + kStep + c, t1 - 1)];
-      nb = pt[min(tb + kStep + 16 + c, t1 - 1)];
+      na = slot_of(p, pt, min(tb + kStep + c, t1 - 1));
+      nb = slot_of(p, pt, min(tb + kStep + 16 + c, t1 - 1));
     }
 
     f32x4 s_a = {0.f, 0.f, 0.f, 0.f}, s_b = {0.f, 0.f, 0.f, 0.f};
@@ -635,6 +651,8 @@ hipError_t launch_paged_decode(const DecodeArgs& a) {
   p.pt_stride = a.pt_stride;
   p.req_rows = a.req_rows;
   p.seq_lens = a.seq_lens;
+  p.slot_max = (uint32_t)min(a.num_slots - 1, (int64_t)INT32_MAX);
+  p.page_mask = (a.page_size > 1 && (a.page_size & (a.page_size - 1)) == 0) ? a.page_size - 1 : 0;
   p.batch = a.batch;
   p.num_q_heads = a.num_q_heads;
   p.ratio = a.num_q_heads / a.num_kv_heads;

@@ -75,6 +75,7 @@ struct ExtendParams {
   int64_t num_slots;
   const int32_t* page_table;
   int64_t pt_stride;
+  int32_t page_mask;       // page_size - 1 for a power-of-two page_size, else 0
   const int32_t* req_rows;
   const int32_t* prefix_lens;
   const int32_t* extend_lens;
@@ -205,9 +206,15 @@ paged_extend_kernel(ExtendParams p) {
   // ring slot t % kPtRing by one 4-byte direct load per lane; the K/V loads
   // of tile t read their slots back from LDS.  Slots are clamped to the pool
   // so that an address can never leave it.
+  // With page_size P > 1 (a power of two) the slots of a page are
+  // consecutive: each lane fetches the entry of its key's page start (the
+  // every-P-th-column view of "Mini-SGLang complete analysis" §4.6.4) and the
+  // offset inside the page is added when the slot is read back.
   int32_t* ring = &pt_ring[w][0][0];
+  const int pmask = p.page_mask;
   auto fetch_pt = [&](int tile) {
-    dma4(pt + min(tile * kBN + lane, kv_end - 1), ring + (tile & (kPtRing - 1)) * kBN);
+    const int key = min(tile * kBN + lane, kv_end - 1);
+    dma4(pt + (key & ~pmask), ring + (tile & (kPtRing - 1)) * kBN);
   };
   auto issue_tile = [&](int tile) {
     const int stg = tile & (kStages - 1);
@@ -218,7 +225,10 @@ paged_extend_kernel(ExtendParams p) {
     // so a read placed after one of them would wait for it
     int32_t slot[kPPW];
 #pragma unroll
-    for (int u = 0; u < kPPW; ++u) slot[u] = rs[4 * (kPPW * w + u) + ld_keyoff];
+    for (int u = 0; u < kPPW; ++u) {
+      const int key = 4 * (kPPW * w + u) + ld_keyoff;
+      slot[u] = rs[key] + (min(tile * kBN + key, kv_end - 1) & pmask);
+    }
 #pragma unroll
     for (int u = 0; u < kPPW; ++u) {
       const int piece = kPPW * w + u;
@@ -494,6 +504,7 @@ hipError_t launch_paged_extend(const ExtendArgs& a) {
   p.num_slots = a.num_slots;
   p.page_table = a.page_table;
   p.pt_stride = a.pt_stride;
+  p.page_mask = (a.page_size > 1 && (a.page_size & (a.page_size - 1)) == 0) ? a.page_size - 1 : 0;
   p.req_rows = a.req_rows;
   p.prefix_lens = a.prefix_lens;
   p.extend_lens = a.extend_lens;

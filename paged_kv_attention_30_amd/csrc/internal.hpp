@@ -72,6 +72,7 @@ struct DecodeArgs {
   int64_t q_stride;
   const void* k_cache;
   const void* v_cache;
+  int64_t num_slots;
   int64_t cache_stride;    // elements between slots
   const int32_t* page_table;
   int64_t pt_stride;

@@ -482,6 +482,39 @@ def test_extend_with_shared_prefix_and_page_size_16():
     assert_close(o16, ro, "extend page16")
 
 
+def test_page_size_16_reads_one_entry_per_page():
+    """At page_size 16 the kernels read only each page's first column of the
+    token table (the every-P-th-column view): with every other column
+    overwritten by out-of-pool values, decode, fused store + decode and
+    extend return the bits they return on the intact table at page_size 1.
+    (A kernel that read a poisoned column would clamp it to the last slot and
+    change the result; it could not leave the pool.)"""
+    banner("page_size 16: one table entry per page")
+    inp = small_extend(91, 32, 8, [(64, 100), (0, 77), (128, 64)], page_size=16,
+                       num_slots=8192, decode_lens=[1000, 17, 512, 300, 16, 33],
+                       shared_prefix=64, shared_by=(0, 2))
+    u = Uploaded(inp)
+    u.store()
+    o1, l1 = u.decode(page_size=1)
+    e1, el1 = u.extend(page_size=1)
+    poisoned = inp.page_table.copy()
+    cols = np.arange(poisoned.shape[1]) % 16 != 0
+    poisoned[:, cols] = inp.num_slots + 1000 + np.arange(int(cols.sum()), dtype=np.int32)
+    u.pt = up(poisoned)
+    o16, l16 = u.decode(page_size=16)
+    e16, el16 = u.extend(page_size=16)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(o16), bits(o1))
+    assert np.array_equal(l16.cpu().numpy().view(np.uint32), l1.cpu().numpy().view(np.uint32))
+    assert np.array_equal(bits(e16), bits(e1))
+    assert np.array_equal(el16.cpu().numpy().view(np.uint32), el1.cpu().numpy().view(np.uint32))
+    kp, vp = oracle_pool(inp)
+    ro, _ = oracle_decode(inp, kp, vp)
+    assert_close(o16, ro, "decode page16 poisoned table")
+    re, _ = oracle_extend(inp, kp, vp)
+    assert_close(e16, re, "extend page16 poisoned table")
+
+
 def test_extend_of_one_token_equals_decode():
     banner("extend(E=1) vs decode")
     inp = small_decode(91, 32, 8, [500, 1, 64, 1300], num_slots=4096)

@@ -67,6 +67,9 @@ CASES = [
     (16, 1, [300, 45], 0, 1, np.int32),
     (32, 2, [90, 1000, 1001], 128, 1, np.int64),
     (32, 8, [160, 33, 1000, 17], 0, 16, np.int32),
+    # GQA ratio 8 in balanced mode (the long-tail batch's launch), lengths
+    # past 4K keys so requests are cut across workgroups
+    (64, 8, [5000, 1024, 7, 2048, 4711, 1300, 64, 3333], 0, 1, np.int64),
 ]
 
 
@@ -74,7 +77,8 @@ CASES = [
 def test_fused_equals_store_then_decode(case):
     hq, hkv, lens, split, ps, ldt = CASES[case]
     banner(f"hq={hq} hkv={hkv} lens={lens} split={split} page_size={ps} out_loc={ldt.__name__}")
-    inp = small_decode(90 + case, hq, hkv, lens, page_size=ps, num_slots=8192)
+    inp = small_decode(90 + case, hq, hkv, lens, page_size=ps,
+                       num_slots=max(8192, -(-2 * sum(lens) // 4096) * 4096))
     d_lens = up(inp.dec_seq_lens)
     a = separate(inp, d_lens, split, ps, ldt)
     b = fused(inp, d_lens, split, ps, ldt)
@@ -113,6 +117,18 @@ def test_fused_more_rows_than_workgroups_and_empty_requests(lens_kind):
     if lens_kind == "empty":
         out = b[1].float().cpu().numpy()
         assert np.all(out[[0, 17, 39]] == 0)
+        assert np.all(np.isneginf(b[2].cpu().numpy()[[0, 17, 39]]))
+    # a spread of requests against the oracle, at the lengths the GPU saw
+    # (the emptied requests are checked above)
+    n = len(lens)
+    picked = {0, 1, 2, n // 3, n // 2, n - 2, n - 1, int(np.argmax(lens))}
+    sel = np.array(sorted(picked - ({0, 17, 39} if lens_kind == "empty" else set())))
+    kp, vp = oracle.store_kv(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.out_loc)
+    ro, rl = oracle.paged_decode(inp.dec_q[sel], kp, vp, inp.page_table, inp.dec_req_rows[sel],
+                                 dl[sel], inp.sm_scale, inp.num_kv_heads)
+    t = torch.from_numpy(sel).cuda()
+    assert_close(b[1][t], ro, f"fused {lens_kind}")
+    assert_lse_close(b[2][t], rl, f"fused {lens_kind}")
 
 
 def test_fused_one_chunk_per_request_and_identity_rows():
@@ -164,3 +180,26 @@ def test_fused_full_c2_in_the_bench_launch():
     t = torch.from_numpy(sel).cuda()
     assert_close(b[1][t], ro, "fused C2")
     assert_lse_close(b[2][t], rl, "fused C2")
+
+
+def test_fused_full_c4_in_the_bench_launch():
+    """The 256-request long-tail batch (Hq 64 / Hkv 8, kv lengths up to 23K)
+    through the one store + decode launch the benchmark times: balanced split,
+    requests cut across workgroups and merged."""
+    banner("fused C4 full size")
+    inp = make_config("C4")
+    d_lens = up(inp.dec_seq_lens)
+    a = separate(inp, d_lens, 0, 1, np.int64)
+    del a[0].k_new, a[0].v_new, a[0].dq
+    b = fused(inp, d_lens, 0, 1, np.int64)
+    assert_same(a, b, "C4")
+    del a
+    torch.cuda.empty_cache()
+    L = inp.dec_seq_lens
+    sel = np.array(sorted({int(np.argmax(L)), int(np.argmin(L)), 0, len(L) - 1, 37, 128, 201}))
+    kp, vp = oracle.store_kv(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.out_loc)
+    ro, rl = oracle.paged_decode(inp.dec_q[sel], kp, vp, inp.page_table, inp.dec_req_rows[sel],
+                                 L[sel], inp.sm_scale, inp.num_kv_heads)
+    t = torch.from_numpy(sel).cuda()
+    assert_close(b[1][t], ro, "fused C4")
+    assert_lse_close(b[2][t], rl, "fused C4")

@@ -5,7 +5,8 @@ definition needs, not what a kernel happens to do:
 
 * decode reads every *distinct* K and V row its requests reference once
   (a slot shared by several requests counts once), walks one 4-byte page
-  table entry per (request, token), reads q and writes the output, and
+  table entry per (request, page) — per token at page_size 1 — reads q and
+  writes the output, and
   writes an fp32 log-sum-exp per (request, q head) when asked to;
 * extend performs two multiply-adds per head dimension for each
   (query, key) pair the causal mask keeps, in each of QK^T and PV;
@@ -25,10 +26,12 @@ def unique_kv_slots(page_table, req_rows, lens) -> int:
 
 
 def decode_bytes(page_table, req_rows, seq_lens, num_q_heads: int, num_kv_heads: int,
-                 head_dim: int, dtype_bytes: int = 2, with_lse: bool = True) -> int:
+                 head_dim: int, dtype_bytes: int = 2, with_lse: bool = True,
+                 page_size: int = 1) -> int:
     B = len(seq_lens)
     kv = unique_kv_slots(page_table, req_rows, seq_lens) * 2 * num_kv_heads * head_dim * dtype_bytes
-    walked = 4 * int(np.sum(np.asarray(seq_lens, dtype=np.int64)))
+    lens = np.asarray(seq_lens, dtype=np.int64)
+    walked = 4 * int(np.sum((lens + page_size - 1) // page_size))
     qo = 2 * B * num_q_heads * head_dim * dtype_bytes
     return kv + walked + qo + (4 * B * num_q_heads if with_lse else 0)
 
