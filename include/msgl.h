@@ -179,6 +179,44 @@ int msgl_store_kv_paged_decode(void* out, float* lse_out, const void* q, int64_t
                                int32_t split_tokens, void* workspace, size_t workspace_bytes,
                                hipStream_t stream);
 
+/* Bytes of device memory that msgl_store_kv_paged_decode_noalloc may use for
+ * its partial results (32 MiB). */
+#define MSGL_DECODE_SCRATCH_BYTES (32u << 20)
+
+/*
+ * msgl_store_kv_paged_decode_noalloc — msgl_store_kv_paged_decode for
+ * callers that cannot allocate device memory or pass a workspace: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation.  The arguments, results and errors are those of
+ * msgl_store_kv_paged_decode without `workspace` / `workspace_bytes`; the
+ * outputs are bit-identical to it.  The partial outputs, partial lse and
+ * per-request workgroup ranges live in one static device array of
+ * MSGL_DECODE_SCRATCH_BYTES inside the library (one copy per GPU, held
+ * until the process ends, its address looked up once per device on the
+ * first call there).  The call allocates and frees nothing and makes no
+ * allocating library call.
+ * Limit: a batch whose partial results need more than
+ * MSGL_DECODE_SCRATCH_BYTES is rejected with MSGL_ERR_WORKSPACE before any
+ * launch (in balanced mode the need is 4 * num_q_heads * (head_dim + 1) *
+ * (resident workgroups + batch) bytes plus 8 per request, about 16.8 MB at
+ * 64 q heads and batch 256 on a 256-CU device).
+ * Every call on one GPU shares that GPU's array and nothing in it needs to
+ * start at any value (each call writes every entry it later reads), but
+ * calls whose work overlaps on one GPU (different streams, or host threads
+ * without ordering) race on it and give undefined results.
+ */
+int msgl_store_kv_paged_decode_noalloc(void* out, float* lse_out, const void* q,
+                                       int64_t q_row_stride, void* k_cache, void* v_cache,
+                                       int64_t num_slots, int64_t cache_row_stride,
+                                       const void* k_new, const void* v_new,
+                                       int64_t new_row_stride, const void* out_loc,
+                                       int32_t index_dtype, const int32_t* page_table,
+                                       int64_t page_table_stride, const int32_t* req_rows,
+                                       const int32_t* seq_lens, int32_t batch,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t page_size, int32_t max_seq_len,
+                                       float sm_scale, int32_t split_tokens, hipStream_t stream);
+
 /* Bytes of workspace msgl_paged_decode needs for these host-side sizes
  * (0 if no request can need more than one chunk).  The split size actually
  * used is written to *split_tokens_out when it is not NULL. */

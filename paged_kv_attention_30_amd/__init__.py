@@ -16,6 +16,7 @@ from .binding import (  # noqa: F401
     store_kv,
     paged_decode,
     store_kv_paged_decode,
+    store_kv_paged_decode_noalloc,
     paged_decode_workspace_size,
     paged_extend,
     paged_extend_workspace_size,

@@ -45,6 +45,11 @@ SIGNATURES = {
                                           _c_void_p, _i32, _c_void_p, _i64, _c_void_p,
                                           _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                           _i32, _c_void_p, _size_t, _c_void_p]),
+    "msgl_store_kv_paged_decode_noalloc": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64,
+                                                  _c_void_p, _c_void_p, _i64, _i64, _c_void_p,
+                                                  _c_void_p, _i64, _c_void_p, _i32, _c_void_p,
+                                                  _i64, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                                  _i32, _i32, _i32, _f32, _i32, _c_void_p]),
     "msgl_paged_decode_workspace_size": (_size_t, [_i32, _i32, _i32, _i32, _i32, _i32,
                                                    ctypes.POINTER(_i32)]),
     "msgl_paged_extend": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p,
@@ -334,8 +339,45 @@ def plan_store_kv_paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
                        d["outputs"], (*d["keep"], k_new, v_new, out_loc))
 
 
+def store_kv_paged_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor,
+                                  v_cache: torch.Tensor, k_new: torch.Tensor,
+                                  v_new: torch.Tensor, out_loc: torch.Tensor,
+                                  page_table: torch.Tensor, seq_lens: torch.Tensor,
+                                  max_seq_len: int, sm_scale: float,
+                                  req_rows: torch.Tensor | None = None, page_size: int = 1,
+                                  split_tokens: int = 0, out: torch.Tensor | None = None,
+                                  lse: torch.Tensor | None = None, want_lse: bool = True,
+                                  stream=None):
+    """:func:`store_kv_paged_decode` through the entry point that takes no
+    workspace: its partial results live in the library's static device
+    scratch (``MSGL_DECODE_SCRATCH_BYTES``), so no device memory is allocated
+    for them.  Calls whose work overlaps on one GPU race on that scratch."""
+    lib = load()
+    d = _decode_args(q, k_cache, v_cache, page_table, seq_lens, max_seq_len, sm_scale, req_rows,
+                     page_size, split_tokens, out, lse, want_lse, None, with_workspace=False)
+    B, hkv, dim = q.shape[0], k_cache.shape[1], k_cache.shape[2]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        _need(t, torch.bfloat16, name, 3)
+        if tuple(t.shape) != (B, hkv, dim) or t.stride(2) != 1 or t.stride(1) != dim:
+            raise ValueError(f"{name} must be [B, Hkv, D] with heads x dims contiguous")
+    if k_new.stride(0) != v_new.stride(0):
+        raise ValueError("k_new and v_new must share a row stride")
+    if out_loc.dtype not in (torch.int32, torch.int64) or not out_loc.is_cuda:
+        raise TypeError("out_loc must be an int32 or int64 GPU tensor")
+    if out_loc.dim() != 1 or out_loc.shape[0] != B or not out_loc.is_contiguous():
+        raise ValueError("out_loc must be a contiguous [B] vector")
+    a = d["args"]
+    # (out, lse, q, q_stride, k, v, slots, cstride) + new rows + (page_table ..
+    # split_tokens), without the workspace pointer and size
+    args = (*a[:8], _ptr(k_new), _ptr(v_new), k_new.stride(0), _ptr(out_loc),
+            INDEX_I64 if out_loc.dtype == torch.int64 else INDEX_I32, *a[8:-2])
+    return PlannedCall(lib.msgl_store_kv_paged_decode_noalloc, args,
+                       "msgl_store_kv_paged_decode_noalloc", d["outputs"],
+                       (*d["keep"], k_new, v_new, out_loc)).run(stream)
+
+
 def _decode_args(q, k_cache, v_cache, page_table, seq_lens, max_seq_len, sm_scale, req_rows,
-                 page_size, split_tokens, out, lse, want_lse, workspace):
+                 page_size, split_tokens, out, lse, want_lse, workspace, with_workspace=True):
     """Checks and marshals the arguments shared by the decode entry points."""
     _need(q, torch.bfloat16, "q", 3)
     n_slots, hkv, d, cstride = _pool_geometry(k_cache, v_cache)
@@ -364,7 +406,7 @@ def _decode_args(q, k_cache, v_cache, page_table, seq_lens, max_seq_len, sm_scal
         if not lse.is_contiguous() or tuple(lse.shape) != (B, hq):
             raise ValueError("lse must be a contiguous [B, Hq] tensor")
     need, _ = paged_decode_workspace_size(B, hq, hkv, max(1, max_seq_len), split_tokens, d)
-    if workspace is None and need:
+    if workspace is None and need and with_workspace:
         workspace = alloc_workspace(need, q.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = (_ptr(out), _ptr(lse), _ptr(q), q.stride(0), _ptr(k_cache), _ptr(v_cache), n_slots,

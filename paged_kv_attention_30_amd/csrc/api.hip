@@ -11,6 +11,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "../../include/msgl.h"
 #include "internal.hpp"
 
@@ -86,8 +88,12 @@ struct DecodeWorkspace {
   size_t total() const { return part_out_bytes + part_lse_bytes + meta_bytes; }
 };
 
+// `grid_rows`: partial rows reserved for the balanced mode's workgroups
+// (kMaxDecodeBlocks for a caller-sized workspace, which must not depend on
+// the device; the launch's own grid for the library's static scratch).
 DecodeWorkspace decode_workspace(int32_t batch, int32_t num_q_heads, int32_t head_dim,
-                                 int32_t max_seq_len, int32_t split_tokens) {
+                                 int32_t max_seq_len, int32_t split_tokens,
+                                 int64_t grid_rows = msgl::kMaxDecodeBlocks) {
   DecodeWorkspace w{0, 0, 0};
   int64_t rows;
   if (split_tokens > 0) {
@@ -95,7 +101,7 @@ DecodeWorkspace decode_workspace(int32_t batch, int32_t num_q_heads, int32_t hea
     if (splits <= 1) return w;
     rows = splits * batch;
   } else {
-    rows = (int64_t)msgl::kMaxDecodeBlocks + batch;
+    rows = grid_rows + batch;
     w.meta_bytes = align256((size_t)batch * 2 * sizeof(int32_t));
   }
   w.part_out_bytes = align256((size_t)rows * num_q_heads * head_dim * sizeof(float));
@@ -221,7 +227,8 @@ int paged_decode_impl(void* out, float* lse_out, const void* q, int64_t q_row_st
                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
                       int32_t max_seq_len, float sm_scale, int32_t split_tokens,
                       void* workspace, size_t workspace_bytes, const FusedStore* fs,
-                      hipStream_t stream, const char* where) {
+                      hipStream_t stream, const char* where,
+                      int64_t grid_rows = msgl::kMaxDecodeBlocks) {
   g_last_error[0] = 0;
   MSGL_CHECK(batch >= 0, MSGL_ERR_SHAPE, "batch %d is negative", batch);
   int st = validate_pool(k_cache, v_cache, num_slots, cache_row_stride, num_kv_heads, head_dim);
@@ -247,7 +254,7 @@ int paged_decode_impl(void* out, float* lse_out, const void* q, int64_t q_row_st
              MSGL_ERR_ALIGN, "int32/fp32 arrays must be 4-byte aligned");
 
   const DecodeWorkspace ws = decode_workspace(batch, num_q_heads, head_dim, max_seq_len,
-                                              split_tokens);
+                                              split_tokens, grid_rows);
   const size_t need = ws.total();
   MSGL_CHECK(workspace_bytes >= need, MSGL_ERR_WORKSPACE, "workspace %zu bytes < required %zu",
              workspace_bytes, need);
@@ -343,6 +350,88 @@ int msgl_store_kv_paged_decode(void* out, float* lse_out, const void* q, int64_t
                            batch, num_q_heads, num_kv_heads, head_dim, page_size, max_seq_len,
                            sm_scale, split_tokens, workspace, workspace_bytes, &fs, stream,
                            "store_kv_paged_decode");
+}
+
+}  // extern "C"
+
+// Device memory of msgl_store_kv_paged_decode_noalloc: the partial outputs,
+// partial lse and per-request workgroup ranges that the caller-provided
+// workspace holds for the other entry points.  Each GPU the library runs on
+// holds one copy until the process ends; host code reaches it only through
+// the address hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MSGL_DECODE_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Address of `scratch` on the current device, looked up once per device.
+int scratch_on_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess)
+    return MSGL_FAIL(MSGL_ERR_LAUNCH, "hipGetDevice failed: %s", hipGetErrorString(e));
+  MSGL_CHECK(dev >= 0 && dev < kMaxDevices, MSGL_ERR_UNSUPPORTED, "device %d beyond %d", dev,
+             kMaxDevices);
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return MSGL_FAIL(MSGL_ERR_LAUNCH, "hipGetSymbolAddress(scratch) failed: %s",
+                       hipGetErrorString(e));
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return MSGL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int msgl_store_kv_paged_decode_noalloc(void* out, float* lse_out, const void* q,
+                                       int64_t q_row_stride, void* k_cache, void* v_cache,
+                                       int64_t num_slots, int64_t cache_row_stride,
+                                       const void* k_new, const void* v_new,
+                                       int64_t new_row_stride, const void* out_loc,
+                                       int32_t index_dtype, const int32_t* page_table,
+                                       int64_t page_table_stride, const int32_t* req_rows,
+                                       const int32_t* seq_lens, int32_t batch,
+                                       int32_t num_q_heads, int32_t num_kv_heads,
+                                       int32_t head_dim, int32_t page_size, int32_t max_seq_len,
+                                       float sm_scale, int32_t split_tokens, hipStream_t stream) {
+  g_last_error[0] = 0;
+  // the split the launch will use sizes the partials: the balanced grid of
+  // this device (one row per workgroup plus one per request) or the chunks
+  MSGL_CHECK(batch >= 0 && num_q_heads > 0 && num_kv_heads > 0 && max_seq_len >= 0 &&
+                 split_tokens >= 0 && head_dim == kHeadDim,
+             MSGL_ERR_SHAPE, "batch, head counts, max_seq_len, split_tokens or head_dim invalid");
+  MSGL_CHECK(ratio_ok(num_q_heads, num_kv_heads), MSGL_ERR_UNSUPPORTED,
+             "num_q_heads %d / num_kv_heads %d: ratio must be 1, 2, 4, 8 or 16", num_q_heads,
+             num_kv_heads);
+  const int64_t grid = split_tokens > 0
+                           ? 0
+                           : msgl::decode_balanced_grid(num_kv_heads, num_q_heads / num_kv_heads,
+                                                        device_compute_units());
+  const size_t need =
+      decode_workspace(batch, num_q_heads, head_dim, max_seq_len, split_tokens, grid).total();
+  MSGL_CHECK(need <= (size_t)MSGL_DECODE_SCRATCH_BYTES, MSGL_ERR_WORKSPACE,
+             "batch %d x %d q heads (max_seq_len %d, split_tokens %d) needs %zu bytes of "
+             "partial results; the library's scratch holds %zu",
+             batch, num_q_heads, max_seq_len, split_tokens, need,
+             (size_t)MSGL_DECODE_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (need) {
+    const int st = scratch_on_device(&ws);
+    if (st) return st;
+  }
+  const FusedStore fs{k_new, v_new, new_row_stride, out_loc, index_dtype};
+  return paged_decode_impl(out, lse_out, q, q_row_stride, k_cache, v_cache, num_slots,
+                           cache_row_stride, page_table, page_table_stride, req_rows, seq_lens,
+                           batch, num_q_heads, num_kv_heads, head_dim, page_size, max_seq_len,
+                           sm_scale, split_tokens, ws, need, &fs, stream,
+                           "store_kv_paged_decode_noalloc", grid);
 }
 
 size_t msgl_paged_extend_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,

@@ -606,12 +606,28 @@ int resident_blocks_per_cu(int ratio) {
   return n;
 }
 
+// Balanced mode: workgroups along x (all resident at once, at most
+// kMaxDecodeBlocks).
+template <int KVB, int NPAR>
+int64_t balanced_grid_x(int num_kv_heads, int ratio, int compute_units) {
+  const int64_t gy = num_kv_heads / KVB;
+  int64_t g = (int64_t)compute_units * resident_blocks_per_cu<KVB, NPAR>(ratio) / gy;
+  if (g < 1) g = 1;
+  if (g > kMaxDecodeBlocks) g = kMaxDecodeBlocks;
+  return g;
+}
+
+template <int KVB>
+int64_t balanced_grid_kvb(int num_kv_heads, int ratio, int compute_units) {
+  if (decode_lds_bytes(KVB, 2, ratio) <= kLdsLimit)
+    return balanced_grid_x<KVB, 2>(num_kv_heads, ratio, compute_units);
+  return balanced_grid_x<KVB, 1>(num_kv_heads, ratio, compute_units);
+}
+
 template <int KVB, int NPAR>
 hipError_t launch_balanced(const DecodeArgs& a, const DecodeParams& p) {
   const unsigned gy = (unsigned)(a.num_kv_heads / KVB);
-  int64_t g = (int64_t)a.balanced_blocks * resident_blocks_per_cu<KVB, NPAR>(p.ratio) / gy;
-  if (g < 1) g = 1;
-  if (g > kMaxDecodeBlocks) g = kMaxDecodeBlocks;
+  const int64_t g = balanced_grid_x<KVB, NPAR>(a.num_kv_heads, p.ratio, a.balanced_blocks);
   hipLaunchKernelGGL((decode_balanced_kernel<KVB, NPAR>), dim3((unsigned)g, gy),
                      dim3(KVB * 64 * NPAR), decode_lds_bytes(KVB, NPAR, p.ratio), a.stream, p);
   return hipGetLastError();
@@ -636,6 +652,15 @@ hipError_t launch_kvb(const DecodeArgs& a, const DecodeParams& p) {
 
 int decode_kv_heads_per_block(int num_kv_heads) {
   return num_kv_heads % 8 == 0 ? 8 : num_kv_heads % 4 == 0 ? 4 : num_kv_heads % 2 == 0 ? 2 : 1;
+}
+
+int64_t decode_balanced_grid(int num_kv_heads, int ratio, int compute_units) {
+  switch (decode_kv_heads_per_block(num_kv_heads)) {
+    case 8: return balanced_grid_kvb<8>(num_kv_heads, ratio, compute_units);
+    case 4: return balanced_grid_kvb<4>(num_kv_heads, ratio, compute_units);
+    case 2: return balanced_grid_kvb<2>(num_kv_heads, ratio, compute_units);
+    default: return balanced_grid_kvb<1>(num_kv_heads, ratio, compute_units);
+  }
 }
 
 hipError_t launch_paged_decode(const DecodeArgs& a) {

@@ -155,6 +155,9 @@ struct MergeArgs {
 constexpr int kMaxDecodeBlocks = 2048;
 
 int decode_kv_heads_per_block(int num_kv_heads);
+// Workgroups the balanced decode launches along x on a device with this
+// many compute units (its partial-output rows are this plus the batch).
+int64_t decode_balanced_grid(int num_kv_heads, int ratio, int compute_units);
 hipError_t launch_store_kv(const StoreArgs& a);
 hipError_t launch_embedding_gather(const GatherArgs& a);
 hipError_t launch_rope_cache(float* cache, int64_t max_position, int32_t rotary_dim, double base,
