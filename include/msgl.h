@@ -405,8 +405,15 @@ int msgl_validate_merge_states(void* out, float* lse_out, const float* part_out,
  * max_bs], padding to the next size with a dummy request on a sentinel page)].
  *
  * A msgl_decode_graph owns one captured HIP graph per ladder size, each
- * holding store_kv + paged_decode (balanced split-KV) for that many rows of
- * fixed-address buffers carved from caller memory `buffer`:
+ * holding the padding of the batch and store_kv + paged_decode (balanced
+ * split-KV) for that many rows of fixed-address buffers carved from caller
+ * memory `buffer`.  With fused_store != 0 the step is captured as
+ * msgl_store_kv_paged_decode (one launch for store + attention), which
+ * needs that call's allocator contract on every replay: out_loc[r] ==
+ * page_table[req_rows[r], seq_lens[r] - 1] and no request's keys include
+ * another request's out_loc (the padded rows all share the sentinel slot,
+ * which they write with the same zero row).  With fused_store == 0 it is
+ * msgl_store_kv followed by msgl_paged_decode, for any table.  Buffers:
  *   q      bf16 [max_bs, num_q_heads, 128]     k_new, v_new  bf16 [max_bs, num_kv_heads, 128]
  *   out    bf16 [max_bs, num_q_heads, 128]     lse           fp32 [max_bs, num_q_heads]
  *   seq_lens, req_rows, out_loc  int32 [max_bs]   then the decode workspace,
@@ -426,10 +433,11 @@ int msgl_validate_merge_states(void* out, float* lse_out, const float* part_out,
  *   the graph lives.
  * create: validates (same rules as the two calls), warms up and captures on a
  *   private stream, synchronises it; allocates the graphs (host/runtime
- *   objects) — a set-up call.  run: two launches (padding + graph), no
- *   allocation, no synchronisation.  Replays on one graph must not overlap
- *   (they share the buffers).  The padding, the graph and the results follow
- *   the stream order of `stream`.
+ *   objects) — a set-up call.  run: sets the padding node's row range on
+ *   the instantiated graph (a host-side update) and launches the graph once;
+ *   no allocation, no synchronisation.  Replays on one graph must not
+ *   overlap (they share the buffers and the graphs).  The padding, the step
+ *   and the results follow the stream order of `stream`.
  */
 typedef struct msgl_decode_graph msgl_decode_graph;
 
@@ -441,8 +449,8 @@ int msgl_decode_graph_create(void* k_cache, void* v_cache, int64_t num_slots,
                              int64_t page_table_stride, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t head_dim, int32_t page_size, int32_t max_bs,
                              int32_t max_seq_len, float sm_scale, int32_t dummy_row,
-                             int32_t sentinel_slot, void* buffer, size_t buffer_bytes,
-                             msgl_decode_graph** out);
+                             int32_t sentinel_slot, int32_t fused_store, void* buffer,
+                             size_t buffer_bytes, msgl_decode_graph** out);
 
 /* batch in [0, max_bs]; 0 enqueues nothing. */
 int msgl_decode_graph_run(msgl_decode_graph* graph, int32_t batch, hipStream_t stream);

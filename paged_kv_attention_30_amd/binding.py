@@ -87,7 +87,7 @@ SIGNATURES = {
                                           _i64, _i32, _i32, _i32]),
     "msgl_decode_graph_layout": (_i32, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_size_t)]),
     "msgl_decode_graph_create": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _i64, _i32,
-                                        _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32,
+                                        _i32, _i32, _i32, _i32, _i32, _f32, _i32, _i32, _i32,
                                         _c_void_p, _size_t, ctypes.POINTER(_c_void_p)]),
     "msgl_decode_graph_run": (_i32, [_c_void_p, _i32, _c_void_p]),
     "msgl_decode_graph_bucket": (_i32, [_c_void_p, _i32]),
@@ -620,17 +620,21 @@ def qk_norm_rope_store(qkv, k_cache, v_cache, positions, cos_sin_cache, out_loc,
 
 
 class DecodeGraph:
-    """Graph-replayed decode step (``msgl_decode_graph_*``): store_kv +
-    paged_decode captured per batch size of the ladder [1, 2, 4, 8, 16, ...,
-    max_bs] over fixed buffers.  Write rows [0, batch) of ``q``, ``k_new``,
-    ``v_new``, ``seq_lens``, ``req_rows``, ``out_loc`` (torch views of the
-    buffer), call ``run(batch)``, read rows [0, batch) of ``out`` / ``lse``.
-    ``page_table[dummy_row, 0]`` must be ``sentinel_slot``, a slot no request
-    owns."""
+    """Graph-replayed decode step (``msgl_decode_graph_*``): padding +
+    store_kv + paged_decode captured per batch size of the ladder [1, 2, 4,
+    8, 16, ..., max_bs] over fixed buffers.  Write rows [0, batch) of ``q``,
+    ``k_new``, ``v_new``, ``seq_lens``, ``req_rows``, ``out_loc`` (torch
+    views of the buffer), call ``run(batch)``, read rows [0, batch) of
+    ``out`` / ``lse``.  ``page_table[dummy_row, 0]`` must be
+    ``sentinel_slot``, a slot no request owns.  ``fused_store``: capture the
+    one-launch store + decode (``msgl_store_kv_paged_decode``), which needs
+    each request's ``out_loc`` to be its own newest key and no other
+    request's key."""
 
     def __init__(self, k_cache: torch.Tensor, v_cache: torch.Tensor, page_table: torch.Tensor,
                  num_q_heads: int, max_bs: int, max_seq_len: int, sm_scale: float,
-                 dummy_row: int, sentinel_slot: int, page_size: int = 1):
+                 dummy_row: int, sentinel_slot: int, page_size: int = 1,
+                 fused_store: bool = False):
         lib = load()
         _need(k_cache, torch.bfloat16, "k_cache", 3)
         _need(page_table, torch.int32, "page_table", 2)
@@ -660,7 +664,8 @@ class DecodeGraph:
         _check(lib.msgl_decode_graph_create(
             k_cache.data_ptr(), v_cache.data_ptr(), slots, k_cache.stride(0),
             page_table.data_ptr(), page_table.stride(0), num_q_heads, hkv, d, page_size, max_bs,
-            max_seq_len, sm_scale, dummy_row, sentinel_slot, self.buffer.data_ptr(),
+            max_seq_len, sm_scale, dummy_row, sentinel_slot, 1 if fused_store else 0,
+            self.buffer.data_ptr(),
             self.buffer.numel(), ctypes.byref(h)), "msgl_decode_graph_create")
         self._h = h
         self.max_bs = max_bs

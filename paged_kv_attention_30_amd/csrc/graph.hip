@@ -12,12 +12,18 @@
 // so the query offsets are a constant arange (here: implicit in the decode
 // call's layout).
 //
-// Here the graph holds the three kernels of one decode step (store_kv,
-// decode, merge).  Before each replay a small fill kernel (not captured: the
-// live batch size changes between replays) turns rows [bs, bucket) into the
+// Here each graph holds one decode step: the padding kernel, then store_kv
+// + decode (+ merge), either as the two library calls or, when the caller's
+// allocator guarantees that a request's new slot is its own newest key and
+// no other request's key (the pages' allocator hands out a fresh slot per
+// new token), as the one store + decode launch the attention layer's forward
+// amounts to (§4.6.7).  The padding kernel turns rows [bs, bucket) into the
 // dummy request: seq_len 1, the caller's dummy page-table row, out_loc = the
-// sentinel slot, zero q / k / v rows.  Every padded row therefore writes the
-// same zero row into the sentinel slot and attends to it alone.
+// sentinel slot, zero q / k / v rows, so every padded row writes the same
+// zero row into the sentinel slot and attends to it alone.  Its row range
+// changes with the live batch size, so before each replay its arguments are
+// set on the instantiated graph (hipGraphExecKernelNodeSetParams, a host-side
+// update): a step is one graph launch.
 
 #include <algorithm>
 #include <new>
@@ -36,6 +42,7 @@ struct msgl_decode_graph {
   int32_t hq = 0, hkv = 0, page_size = 1, max_bs = 0, max_seq_len = 0;
   float sm_scale = 0.f;
   int32_t dummy_row = 0, sentinel_slot = 0;
+  int32_t fused = 0;                    // capture msgl_store_kv_paged_decode
   char* q = nullptr;
   char* k_new = nullptr;
   char* v_new = nullptr;
@@ -49,19 +56,22 @@ struct msgl_decode_graph {
   std::vector<int32_t> ladder;          // ascending
   std::vector<hipGraph_t> graphs;       // per ladder entry
   std::vector<hipGraphExec_t> execs;
+  std::vector<hipGraphNode_t> pad_nodes; // the padding kernel of each graph
 };
 
 namespace {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// rows [r0, r1) of the fixed buffers become the dummy request
+// rows [r0, r1) of the fixed buffers become the dummy request (workgroup i
+// takes row r0 + i; r0 == r1: nothing)
 __global__ void __launch_bounds__(256) pad_rows_kernel(char* q, char* k_new, char* v_new,
                                                        int32_t* seq_lens, int32_t* req_rows,
-                                                       int32_t* out_loc, int32_t r0, int32_t hq,
-                                                       int32_t hkv, int32_t dummy_row,
+                                                       int32_t* out_loc, int32_t r0, int32_t r1,
+                                                       int32_t hq, int32_t hkv, int32_t dummy_row,
                                                        int32_t sentinel) {
   const int32_t r = r0 + (int32_t)blockIdx.x;
+  if (r >= r1) return;
   const int64_t qb = (int64_t)hq * 128 * 2;     // bytes of one q row
   const int64_t kb = (int64_t)hkv * 128 * 2;    // bytes of one k / v row
   const uint4 z = {0u, 0u, 0u, 0u};
@@ -78,16 +88,44 @@ __global__ void __launch_bounds__(256) pad_rows_kernel(char* q, char* k_new, cha
   }
 }
 
+// Launch of the padding kernel for rows [r0, r1) (at least one workgroup,
+// so the node exists in every captured graph), or its node parameters.
+struct PadLaunch {
+  void* args[12];
+  char* q;
+  char* k_new;
+  char* v_new;
+  int32_t* seq_lens;
+  int32_t* req_rows;
+  int32_t* out_loc;
+  int32_t r0, r1, hq, hkv, dummy_row, sentinel;
+  PadLaunch(const msgl_decode_graph* g, int32_t a, int32_t b)
+      : q(g->q), k_new(g->k_new), v_new(g->v_new), seq_lens(g->seq_lens),
+        req_rows(g->req_rows), out_loc(g->out_loc), r0(a), r1(b), hq(g->hq), hkv(g->hkv),
+        dummy_row(g->dummy_row), sentinel(g->sentinel_slot) {
+    void* a12[12] = {&q, &k_new, &v_new, &seq_lens, &req_rows, &out_loc, &r0, &r1, &hq, &hkv,
+                     &dummy_row, &sentinel};
+    for (int i = 0; i < 12; ++i) args[i] = a12[i];
+  }
+  unsigned blocks() const { return (unsigned)std::max(1, r1 - r0); }
+};
+
 hipError_t pad(const msgl_decode_graph* g, int32_t r0, int32_t r1, hipStream_t s) {
-  if (r1 <= r0) return hipSuccess;
-  hipLaunchKernelGGL(pad_rows_kernel, dim3((unsigned)(r1 - r0)), dim3(256), 0, s, g->q, g->k_new,
-                     g->v_new, g->seq_lens, g->req_rows, g->out_loc, r0, g->hq, g->hkv,
-                     g->dummy_row, g->sentinel_slot);
+  PadLaunch l(g, r0, r1);
+  hipLaunchKernelGGL(pad_rows_kernel, dim3(l.blocks()), dim3(256), 0, s, l.q, l.k_new, l.v_new,
+                     l.seq_lens, l.req_rows, l.out_loc, l.r0, l.r1, l.hq, l.hkv, l.dummy_row,
+                     l.sentinel);
   return hipGetLastError();
 }
 
-// the captured step for a batch of bs rows
+// the step for a batch of bs rows (after the padding)
 int step(const msgl_decode_graph* g, int32_t bs, hipStream_t s) {
+  if (g->fused)
+    return msgl_store_kv_paged_decode(
+        g->out, g->lse, g->q, (int64_t)g->hq * 128, g->k_cache, g->v_cache, g->num_slots,
+        g->cache_row_stride, g->k_new, g->v_new, (int64_t)g->hkv * 128, g->out_loc,
+        MSGL_INDEX_I32, g->page_table, g->pt_stride, g->req_rows, g->seq_lens, bs, g->hq, g->hkv,
+        128, g->page_size, g->max_seq_len, g->sm_scale, 0, g->ws, g->ws_bytes, s);
   int st = msgl_store_kv(g->k_cache, g->v_cache, g->num_slots, g->cache_row_stride, g->k_new,
                          g->v_new, (int64_t)g->hkv * 128, g->out_loc, MSGL_INDEX_I32, bs, g->hkv,
                          128, MSGL_DTYPE_BF16, s);
@@ -96,6 +134,23 @@ int step(const msgl_decode_graph* g, int32_t bs, hipStream_t s) {
                            g->num_slots, g->cache_row_stride, g->page_table, g->pt_stride,
                            g->req_rows, g->seq_lens, bs, g->hq, g->hkv, 128, g->page_size,
                            g->max_seq_len, g->sm_scale, 0, g->ws, g->ws_bytes, s);
+}
+
+// The padding kernel's node in a captured graph (null if not found).
+hipGraphNode_t find_pad_node(hipGraph_t gr) {
+  size_t n = 0;
+  if (hipGraphGetNodes(gr, nullptr, &n) != hipSuccess || n == 0) return nullptr;
+  std::vector<hipGraphNode_t> nodes(n);
+  if (hipGraphGetNodes(gr, nodes.data(), &n) != hipSuccess) return nullptr;
+  for (hipGraphNode_t nd : nodes) {
+    hipGraphNodeType t;
+    if (hipGraphNodeGetType(nd, &t) != hipSuccess || t != hipGraphNodeTypeKernel) continue;
+    hipKernelNodeParams kp;
+    if (hipGraphKernelNodeGetParams(nd, &kp) == hipSuccess &&
+        kp.func == reinterpret_cast<const void*>(pad_rows_kernel))
+      return nd;
+  }
+  return nullptr;
 }
 
 void release(msgl_decode_graph* g) {
@@ -141,8 +196,8 @@ int msgl_decode_graph_create(void* k_cache, void* v_cache, int64_t num_slots,
                              int64_t page_table_stride, int32_t num_q_heads, int32_t num_kv_heads,
                              int32_t head_dim, int32_t page_size, int32_t max_bs,
                              int32_t max_seq_len, float sm_scale, int32_t dummy_row,
-                             int32_t sentinel_slot, void* buffer, size_t buffer_bytes,
-                             msgl_decode_graph** out) {
+                             int32_t sentinel_slot, int32_t fused_store, void* buffer,
+                             size_t buffer_bytes, msgl_decode_graph** out) {
   if (!out) return MSGL_ERR_NULL;
   *out = nullptr;
   if (!k_cache || !v_cache || !page_table || !buffer) return MSGL_ERR_NULL;
@@ -169,6 +224,7 @@ int msgl_decode_graph_create(void* k_cache, void* v_cache, int64_t num_slots,
   g->sm_scale = sm_scale;
   g->dummy_row = dummy_row;
   g->sentinel_slot = sentinel_slot;
+  g->fused = fused_store ? 1 : 0;
   char* b = (char*)buffer;
   g->q = b + off[0];
   g->k_new = b + off[1];
@@ -194,6 +250,7 @@ int msgl_decode_graph_create(void* k_cache, void* v_cache, int64_t num_slots,
   st = MSGL_OK;
   g->graphs.assign(g->ladder.size(), nullptr);
   g->execs.assign(g->ladder.size(), nullptr);
+  g->pad_nodes.assign(g->ladder.size(), nullptr);
   if (pad(g, 0, max_bs, s) != hipSuccess) st = MSGL_ERR_LAUNCH;
   for (int i = (int)g->ladder.size() - 1; i >= 0 && st == MSGL_OK; --i) {
     const int32_t bs = g->ladder[i];
@@ -203,7 +260,9 @@ int msgl_decode_graph_create(void* k_cache, void* v_cache, int64_t num_slots,
       st = MSGL_ERR_LAUNCH;
       break;
     }
-    const int cst = step(g, bs, s);
+    // the padding node (captured with an empty row range; set per replay)
+    const hipError_t pe = pad(g, bs, bs, s);
+    const int cst = pe == hipSuccess ? step(g, bs, s) : MSGL_ERR_LAUNCH;
     hipGraph_t gr = nullptr;
     const hipError_t e = hipStreamEndCapture(s, &gr);
     g->graphs[i] = gr;
@@ -211,7 +270,9 @@ int msgl_decode_graph_create(void* k_cache, void* v_cache, int64_t num_slots,
       st = cst != MSGL_OK ? cst : MSGL_ERR_LAUNCH;
       break;
     }
-    if (hipGraphInstantiate(&g->execs[i], gr, nullptr, nullptr, 0) != hipSuccess) {
+    g->pad_nodes[i] = find_pad_node(gr);
+    if (!g->pad_nodes[i] ||
+        hipGraphInstantiate(&g->execs[i], gr, nullptr, nullptr, 0) != hipSuccess) {
       st = MSGL_ERR_LAUNCH;
       break;
     }
@@ -231,7 +292,16 @@ int msgl_decode_graph_run(msgl_decode_graph* g, int32_t batch, hipStream_t strea
   if (batch < 0 || batch > g->max_bs) return MSGL_ERR_SHAPE;
   if (batch == 0) return MSGL_OK;
   const size_t i = std::lower_bound(g->ladder.begin(), g->ladder.end(), batch) - g->ladder.begin();
-  if (pad(g, batch, g->ladder[i], stream) != hipSuccess) return MSGL_ERR_LAUNCH;
+  PadLaunch l(g, batch, g->ladder[i]);
+  hipKernelNodeParams kp = {};
+  kp.func = reinterpret_cast<void*>(pad_rows_kernel);
+  kp.gridDim = dim3(l.blocks());
+  kp.blockDim = dim3(256);
+  kp.sharedMemBytes = 0;
+  kp.kernelParams = l.args;
+  kp.extra = nullptr;
+  if (hipGraphExecKernelNodeSetParams(g->execs[i], g->pad_nodes[i], &kp) != hipSuccess)
+    return MSGL_ERR_LAUNCH;
   if (hipGraphLaunch(g->execs[i], stream) != hipSuccess) return MSGL_ERR_LAUNCH;
   return MSGL_OK;
 }

@@ -290,7 +290,7 @@ def test_decode_graph_layout_rule(lib):
     assert lib.msgl_decode_graph_layout(4, 32, 8, 128, 4096, None) == SHAPE
     h = ctypes.c_void_p()
     assert lib.msgl_decode_graph_create(None, None, 0, 0, None, 0, 32, 8, 128, 1, 4, 64, 0.1, 0, 0,
-                                        None, 0, ctypes.byref(h)) == NULL
+                                        0, None, 0, ctypes.byref(h)) == NULL
     assert lib.msgl_decode_graph_run(None, 1, None) == NULL
     assert lib.msgl_decode_graph_bucket(None, 1) == -1
 
