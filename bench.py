@@ -650,6 +650,19 @@ def graph_run(steps: int, warmup: int):
     return {"workload": WORKLOAD_TEXT["GRAPH"], "per_batch": res}
 
 
+def decode_kernel_label(inp, split_used: int) -> str:
+    """Name of the decode kernel instance a call launches, by the library's own rule: kv
+    heads per workgroup = largest of 8 / 4 / 2 / 1 dividing Hkv; balanced split (two waves
+    per kv head when their LDS fits in 160 KiB) unless a fixed chunk size is used."""
+    hkv, ratio = inp.num_kv_heads, inp.num_q_heads // inp.num_kv_heads
+    kvb = next(k for k in (8, 4, 2, 1) if hkv % k == 0)
+    if split_used > 0:
+        return f"decode_fixed_kernel<{kvb}>"
+    wave_lds = 32 * 128 + 64                     # V tile + hand-over slot, bf16 elements
+    lds2 = (kvb * 2 * wave_lds + kvb * ratio * 128) * 2
+    return f"decode_balanced_kernel<{kvb}, {2 if lds2 <= 160 * 1024 else 1}>"
+
+
 def store_bytes_of(inp):
     """store_kv moves each new K and V row in and out once, plus its int64 index."""
     n_new = int(inp.out_loc.shape[0])
@@ -798,9 +811,10 @@ def main(argv=None) -> int:
                 "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "traffic": traffic,
-                "kernel": ("decode_balanced_kernel<8, 2> (store_kv fused) + merge_kernel "
-                           "(one msgl_store_kv_paged_decode call)" if run.fused else
-                           "decode_balanced_kernel<8, 2> + merge_kernel (one msgl_paged_decode call)"),
+                "kernel": (f"{decode_kernel_label(inp, run.split_used)} (store_kv fused) + "
+                           "merge_kernel (one msgl_store_kv_paged_decode call)" if run.fused else
+                           f"{decode_kernel_label(inp, run.split_used)} + merge_kernel "
+                           "(one msgl_paged_decode call)"),
                 "alg_bytes_per_launch": alg, "avg_launch_ms": round(dec_ms, 4)}
     fused = run.fused
     del run
