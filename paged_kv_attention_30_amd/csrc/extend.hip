@@ -121,6 +121,10 @@ constexpr int kPPW = kPieces / kWaves;   // 1-KiB pieces each wave loads per K (
 // the same unit at the same time.  A wave raises its issue priority while it
 // issues MFMAs (S = K Q^T, O += P V) and drops it for the softmax, so the
 // SIMD feeds the matrix unit first and fills the gaps with vector work.
+// kPageOffsets: page_size > 1 (a power of two), so keys add their offset
+// inside the page to the entry of the page's first column; the page_size 1
+// instance drops that arithmetic from the load path.
+template <bool kPageOffsets>
 __global__ void __launch_bounds__(kWaves * 64, 1)
 paged_extend_kernel(ExtendParams p) {
   // stage t % kStages holds the K and V of tile t
@@ -195,9 +199,10 @@ paged_extend_kernel(ExtendParams p) {
   // 4I + l/16 at physical 16-byte position l % 16, i.e. K chunk
   // (l%16) ^ (key & 15) and V 16-byte unit (l%16) ^ (4 * (key & 3)).
   // row offsets in 32 x 32 -> 64-bit arithmetic (the host checks that the
-  // row stride fits 32 bits); slots clamp to the pool
+  // row stride fits 32 bits); slots clamp to the pool (an unsigned minimum:
+  // a negative entry takes the last slot)
   const uint32_t cs32 = (uint32_t)p.cache_stride_bytes;
-  const int slot_max = (int)min(p.num_slots - 1, (int64_t)INT32_MAX);
+  const uint32_t slot_max = (uint32_t)min(p.num_slots - 1, (int64_t)INT32_MAX);
   const char* kbase = p.k_cache + (int64_t)g * kHeadDim * 2;
   const int64_t v_minus_k = p.v_cache - p.k_cache;
   const int ld_keyoff = lane >> 4;     // key within a piece
@@ -211,7 +216,7 @@ paged_extend_kernel(ExtendParams p) {
   // every-P-th-column view of "Mini-SGLang complete analysis" §4.6.4) and the
   // offset inside the page is added when the slot is read back.
   int32_t* ring = &pt_ring[w][0][0];
-  const int pmask = p.page_mask;
+  const int pmask = kPageOffsets ? p.page_mask : 0;
   auto fetch_pt = [&](int tile) {
     const int key = min(tile * kBN + lane, kv_end - 1);
     dma4(pt + (key & ~pmask), ring + (tile & (kPtRing - 1)) * kBN);
@@ -233,7 +238,7 @@ paged_extend_kernel(ExtendParams p) {
     for (int u = 0; u < kPPW; ++u) {
       const int piece = kPPW * w + u;
       const int key = 4 * piece + ld_keyoff;       // key within the tile
-      const uint32_t sl = (uint32_t)min(max(slot[u], 0), slot_max);
+      const uint32_t sl = min((uint32_t)slot[u], slot_max);
       const char* rowp = kbase + (uint64_t)sl * cs32;
       const int kchunk = ld_phys ^ (key & 15);
       const int vunit = ld_phys ^ (4 * (key & 3));
@@ -540,7 +545,12 @@ hipError_t launch_paged_extend(const ExtendArgs& a) {
     p.work_list = pp.list;
   }
   const int64_t blocks = (int64_t)p.n_qtiles * a.batch * a.num_kv_heads;
-  hipLaunchKernelGGL(paged_extend_kernel, dim3((unsigned)blocks), dim3(kWaves * 64), 0, a.stream, p);
+  if (p.page_mask)
+    hipLaunchKernelGGL(paged_extend_kernel<true>, dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+                       a.stream, p);
+  else
+    hipLaunchKernelGGL(paged_extend_kernel<false>, dim3((unsigned)blocks), dim3(kWaves * 64), 0,
+                       a.stream, p);
   return hipGetLastError();
 }
 
