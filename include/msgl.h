@@ -240,12 +240,14 @@ size_t msgl_paged_decode_workspace_size(int32_t batch, int32_t num_q_heads,
  *   causal     must be 1 (the only mode the method uses)
  *   workspace  optional, device memory of at least
  *              msgl_paged_extend_workspace_size(...) bytes, 16-byte aligned,
- *              owned by the caller and overwritten by the call.  With it, a
- *              planning pass orders the (request, query tile) work items
- *              longest first before the attention pass; with NULL the items
- *              run last query tile first.  The results are bit-identical
- *              either way; only the load balance differs.  A non-NULL
- *              workspace smaller than required is MSGL_ERR_WORKSPACE.
+ *              owned by the caller and overwritten by the call.  With it and
+ *              batch > 1, a planning pass orders the (request, query tile)
+ *              work items longest first before the attention pass; with
+ *              NULL (or one request, whose tiles are already in that order)
+ *              the items run last query tile first.  The results are
+ *              bit-identical either way; only the load balance differs.  A
+ *              non-NULL workspace smaller than required is
+ *              MSGL_ERR_WORKSPACE.
  */
 int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_stride,
                       const void* k_cache, const void* v_cache, int64_t num_slots,

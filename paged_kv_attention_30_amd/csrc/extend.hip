@@ -528,7 +528,9 @@ hipError_t launch_paged_extend(const ExtendArgs& a) {
   p.work_count = nullptr;
   p.work_list = nullptr;
   if (a.batch == 0 || p.n_qtiles == 0) return hipSuccess;
-  if (a.workspace) {
+  // a single request's query tiles already run longest first in the natural
+  // order (later tiles see more keys), so it is not planned
+  if (a.workspace && a.batch > 1) {
     PlanParams pp;
     pp.prefix_lens = a.prefix_lens;
     pp.extend_lens = a.extend_lens;
