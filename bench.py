@@ -34,6 +34,7 @@ if ROOT not in sys.path:
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+EXTRA_WARM_S = 0.5              # untimed warm-up per extra workload (seconds of its own steps)
 METRIC = "paged decode KV GB/s + extend TFLOP/s on 1 MI355X, % of roofline"
 # every library source and the public headers: a stored traffic figure is
 # used only while none of them has changed since the counters were taken
@@ -208,8 +209,14 @@ class Run:
         torch.cuda.synchronize()
 
 
-def timed_steps(run: Run, steps: int, warmup: int, graphs: bool = False):
+def timed_steps(run: Run, steps: int, warmup: int, graphs: bool = False,
+                min_warm_s: float = 0.0):
     """Warm up, then time exactly ``steps`` whole steps, then each phase alone.
+
+    Warm-up is ``warmup`` steps, continued (when ``min_warm_s`` > 0) until
+    that many seconds of steps have run: after seconds of host-side input
+    generation the GPU idles down, and a few steps do not bring its clock
+    back (the extend read 12-14% slower after 3 warm-up steps than after 50).
 
     The steps are bracketed by two HIP events only (an event recorded between
     two kernels leaves the GPU idle for several microseconds, so none sits
@@ -229,9 +236,14 @@ def timed_steps(run: Run, steps: int, warmup: int, graphs: bool = False):
         for c in order:
             calls[c]()
 
+    w0 = time.perf_counter()
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    while time.perf_counter() - w0 < min_warm_s:
+        for _ in range(10):
+            step()
+        torch.cuda.synchronize()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -830,8 +842,9 @@ def main(argv=None) -> int:
             continue
         inp_x = make_config(name)
         run_x = Run(inp_x, args.split_tokens, not args.separate_store)
-        res_x = timed_steps(run_x, max(5, args.steps // 5), 3, args.graphs)
-        extras[name] = summarize(name, inp_x, run_x, res_x, max(5, args.steps // 5))
+        n_x = max(10, args.steps // 5)
+        res_x = timed_steps(run_x, n_x, 3, args.graphs, min_warm_s=EXTRA_WARM_S)
+        extras[name] = summarize(name, inp_x, run_x, res_x, n_x)
         del run_x
         torch.cuda.empty_cache()
 
