@@ -550,3 +550,79 @@ def test_extend_chunked_equals_full_prefill():
         torch.cuda.synchronize()
         assert_close(oc, ro[a:b], f"chunk {a}:{b}")
         assert np.abs(f64(oc) - f64(full[a:b])).max() <= 2e-2
+
+
+# ---------------------------------------------------------------------------
+# sizes at the edges of the work split
+# ---------------------------------------------------------------------------
+
+def test_decode_one_request_cut_across_every_workgroup():
+    """One request of 65,536 keys with the balanced split: its key line is
+    cut into one range per workgroup, so the merge folds one partial per
+    workgroup (eight at a time, many batches); also the fixed split at 512
+    keys (128 chunks)."""
+    banner("decode one 65,536-key request, balanced and fixed")
+    inp = small_decode(140, 32, 8, [65536], num_slots=131072)
+    u = Uploaded(inp)
+    u.store()
+    ob, lb = u.decode(split_tokens=0)
+    of, lf = u.decode(split_tokens=512)
+    torch.cuda.synchronize()
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle_decode(inp, kp, vp)
+    assert_close(ob, ro, "decode 64K balanced")
+    assert_lse_close(lb, rl, "decode 64K balanced lse")
+    assert_close(of, ro, "decode 64K fixed 512")
+    assert_lse_close(lf, rl, "decode 64K fixed 512 lse")
+
+
+def test_decode_thousands_of_tiny_requests():
+    """4,000 requests of 1-40 keys (a few empty): every workgroup's range
+    holds dozens of request segments, most finished inside one workgroup,
+    some cut at range ends."""
+    banner("decode 4,000 tiny requests")
+    rng = np.random.default_rng(141)
+    lens = rng.integers(1, 41, 4000)
+    inp = small_decode(141, 32, 8, lens, num_slots=262144)
+    dl = inp.dec_seq_lens.copy()
+    dl[[5, 1999, 3999]] = 0
+    u = Uploaded(inp)
+    u.store()
+    out, lse = msgl.paged_decode(u.dq, u.k, u.v, u.pt, up(dl), u.d_max, inp.sm_scale,
+                                 req_rows=u.d_rows, split_tokens=0)
+    torch.cuda.synchronize()
+    got = f64(out)
+    assert np.all(got[[5, 1999, 3999]] == 0)
+    assert np.all(np.isneginf(lse.cpu().numpy()[[5, 1999, 3999]]))
+    sel = np.array(sorted(set(rng.choice(4000, 48, replace=False).tolist()) - {5, 1999, 3999}
+                          | {0, 1, 2000, 3998}))
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle.paged_decode(inp.dec_q[sel], kp, vp, inp.page_table, inp.dec_req_rows[sel],
+                                 dl[sel], inp.sm_scale, inp.num_kv_heads)
+    t = torch.from_numpy(sel).cuda()
+    assert_close(out[t], ro, "decode 4,000 tiny requests")
+    assert_lse_close(lse[t], rl, "decode 4,000 tiny requests lse")
+
+
+def test_extend_prefix_past_1024_key_tiles():
+    """A 66,000-key prefix: its query tile visits 1,033 key tiles, more than
+    the planner has length buckets, so the planner sorts by coarser buckets;
+    planned and natural orders bitwise equal, sampled rows against the
+    oracle (the long request and the short one)."""
+    banner("extend with a 66,000-key prefix")
+    inp = small_extend(142, 32, 8, [(66000, 70), (10, 300)], num_slots=131072)
+    u = Uploaded(inp)
+    u.store()
+    op, lp = u.extend(plan=True)
+    on, ln = u.extend(plan=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(op), bits(on))
+    assert np.array_equal(lp.cpu().numpy().view(np.uint32), ln.cpu().numpy().view(np.uint32))
+    rows = [0, 1, 33, 63, 64, 69, 70, 71, 200, 369]
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle.paged_extend(inp.ext_q, kp, vp, inp.page_table, inp.ext_req_rows,
+                                 inp.ext_prefix_lens, inp.ext_extend_lens, inp.ext_q_offsets,
+                                 inp.sm_scale, inp.num_kv_heads, query_subset=rows)
+    t = torch.tensor(rows, device="cuda")
+    assert_close(op[t], ro[rows], "extend 66K prefix")
+    assert_lse_close(lp[t], rl[rows], "extend 66K prefix lse")
