@@ -53,9 +53,23 @@
  *   are bit-identical to passing P = 1 for the same table.
  * - Lengths and indices that live in device memory (seq_lens, prefix_lens,
  *   extend_lens, q_offsets, req_rows, page_table entries, out_loc) are NOT
- *   range-checked: out-of-range values are undefined behaviour, as in the
- *   pages' kernels.  Host-side scalars and pointers ARE validated before any
- *   HIP call; a rejected call enqueues nothing.
+ *   range-checked in the release library: out-of-range values are undefined
+ *   behaviour, as in the pages' kernels.  Host-side scalars and pointers ARE
+ *   validated before any HIP call; a rejected call enqueues nothing.
+ * - The debug-check library (libmsgl_debug.so, the same sources built with
+ *   MSGL_DEBUG_CHECKS; msgl_debug_checks() returns 1 there) also checks them
+ *   on the device before each store, decode, extend and prologue call: out_loc
+ *   entries in [0, num_slots); lengths non-negative, within their declared
+ *   maxima (max_seq_len, max_extend_len, max_kv_len) and the page-table width;
+ *   q_offsets steps equal to extend_len; req_rows entries non-negative; every
+ *   page-table entry the call would read inside the pool; for the fused store
+ *   + decode, out_loc[r] equal to the slot of request r's newest key.  The
+ *   check runs on the call's stream and the call WAITS for it (a debug
+ *   build); on failure the call launches nothing else and returns
+ *   MSGL_ERR_INDEX with the first offending request, key and value in
+ *   msgl_last_error().  Not checked: that out_loc entries are distinct, and a
+ *   req_rows entry past the last table row (no row count crosses the ABI).
+ *   Under stream capture the checks are skipped (nothing may wait there).
  * - Return value: MSGL_OK (0) or a negative msgl_status.  No exception crosses
  *   the ABI.  msgl_last_error() returns a thread-local message for the last
  *   failure on the calling thread (including the source location).
@@ -78,7 +92,8 @@ typedef enum msgl_status {
   MSGL_ERR_UNSUPPORTED = -3,  /* dtype, head_dim, ratio or page_size not served */
   MSGL_ERR_ALIGN = -4,        /* pointer or stride breaks required alignment    */
   MSGL_ERR_WORKSPACE = -5,    /* workspace missing or smaller than required     */
-  MSGL_ERR_LAUNCH = -6        /* the HIP runtime rejected a kernel launch       */
+  MSGL_ERR_LAUNCH = -6,       /* the HIP runtime rejected a kernel launch       */
+  MSGL_ERR_INDEX = -7         /* debug-check build: device index out of range   */
 } msgl_status;
 
 enum { MSGL_DTYPE_BF16 = 0, MSGL_DTYPE_F32 = 1 };
@@ -86,6 +101,10 @@ enum { MSGL_INDEX_I32 = 0, MSGL_INDEX_I64 = 1 };
 
 /* Library version as major*10000 + minor*100 + patch. */
 int msgl_version(void);
+
+/* 1 in the debug-check library (device indices checked before each call,
+ * see above), 0 in the release library. */
+int msgl_debug_checks(void);
 
 /* Static text for a status code. */
 const char* msgl_status_string(int status);

@@ -2,7 +2,9 @@
 
 Compiles every ``csrc/*.hip`` translation unit (hipcc) and every host-only
 ``csrc/*.cpp`` one (g++) in parallel into ``_build/`` and links them into
-``paged_kv_attention_30_amd/libmsgl.so``.
+``paged_kv_attention_30_amd/libmsgl.so``; the same sources with
+MSGL_DEBUG_CHECKS defined (device-side index checks before each call) into
+``_build/debug/`` and ``libmsgl_debug.so``.
 Always recompiles (the caller asked for a build).
 """
 
@@ -20,6 +22,7 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB_NAME = "libmsgl.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+DEBUG_LIB_PATH = os.path.join(PKG_DIR, "libmsgl_debug.so")
 ARCH = os.environ.get("MSGL_OFFLOAD_ARCH", "gfx950")
 
 COMMON_FLAGS = [
@@ -67,27 +70,37 @@ def _run(cmd: list[str]) -> None:
         sys.stderr.write("\n".join(lines) + "\n")
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build_variant(debug: bool, verbose: bool = False) -> str:
+    out_dir = os.path.join(BUILD, "debug") if debug else BUILD
+    lib_path = DEBUG_LIB_PATH if debug else LIB_PATH
+    defines = ["-DMSGL_DEBUG_CHECKS"] if debug else []
+    os.makedirs(out_dir, exist_ok=True)
     cc = hipcc()
     objs = []
     cmds = []
     for src in sources():
         stem, ext = os.path.splitext(os.path.basename(src))
-        obj = os.path.join(BUILD, stem + ".o")
+        obj = os.path.join(out_dir, stem + ".o")
         objs.append(obj)
         if ext == ".cpp":
-            cmds.append([host_cxx(), *HOST_FLAGS, "-c", src, "-o", obj])
+            cmds.append([host_cxx(), *HOST_FLAGS, *defines, "-c", src, "-o", obj])
         else:
-            cmds.append([cc, *COMMON_FLAGS, "-c", src, "-o", obj])
+            cmds.append([cc, *COMMON_FLAGS, *defines, "-c", src, "-o", obj])
     with ThreadPoolExecutor(min(8, len(cmds))) as ex:
         list(ex.map(_run, cmds))
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, lib_path)
     if verbose:
-        print(f"built {LIB_PATH}")
-    return LIB_PATH
+        print(f"built {lib_path}")
+    return lib_path
+
+
+def build(verbose: bool = False) -> str:
+    """Both libraries; returns the release one's path."""
+    path = build_variant(False, verbose)
+    build_variant(True, verbose)
+    return path
 
 
 if __name__ == "__main__":

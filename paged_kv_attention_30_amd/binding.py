@@ -9,12 +9,13 @@ If the library is missing, loading fails loudly: there is no fallback.
 
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
 import torch
 
-from ._build import LIB_PATH
+from ._build import DEBUG_LIB_PATH, LIB_PATH
 
 MSGL_OK = 0
 DTYPE_BF16 = 0
@@ -32,6 +33,7 @@ _size_t = ctypes.c_size_t
 
 SIGNATURES = {
     "msgl_version": (_i32, []),
+    "msgl_debug_checks": (_i32, []),
     "msgl_status_string": (ctypes.c_char_p, [_i32]),
     "msgl_last_error": (ctypes.c_char_p, []),
     "msgl_store_kv": (_i32, [_c_void_p, _c_void_p, _i64, _i64, _c_void_p, _c_void_p, _i64,
@@ -119,6 +121,19 @@ def load(path: str | None = None):
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+@contextlib.contextmanager
+def using_library(path: str):
+    """Route the calls made inside the block through the library at ``path``
+    (e.g. DEBUG_LIB_PATH, the debug-check build); the previous one afterwards."""
+    global _lib
+    saved = _lib
+    _lib = None
+    try:
+        yield load(path)
+    finally:
+        _lib = saved
 
 
 def _check(status: int, where: str) -> None:

@@ -64,6 +64,65 @@ int launch_status(hipError_t e, const char* what) {
   return MSGL_FAIL(MSGL_ERR_LAUNCH, "%s launch failed: %s", what, hipGetErrorString(e));
 }
 
+#ifdef MSGL_DEBUG_CHECKS
+// Debug-check build: waits for the checks queued on `s` and turns the first
+// failure into MSGL_ERR_INDEX with its details (the call's own kernels are
+// then not launched).
+int debug_verdict(hipStream_t s, const char* where) {
+  msgl::DebugFailure f;
+  const hipError_t e = msgl::debug_collect(s, &f);
+  if (e != hipSuccess)
+    return MSGL_FAIL(MSGL_ERR_LAUNCH, "%s: index checks did not run: %s", where,
+                     hipGetErrorString(e));
+  if (f.bits == 0) return MSGL_OK;
+  switch (f.first) {
+    case msgl::kDebugOutLoc:
+      return MSGL_FAIL(MSGL_ERR_INDEX, "%s: out_loc[%d] = %lld is outside [0, num_slots) "
+                       "(failed checks 0x%x)", where, f.a, f.v, f.bits);
+    case msgl::kDebugLength:
+      return MSGL_FAIL(MSGL_ERR_INDEX, "%s: request %d: length %lld (extend_len %d) is negative, "
+                       "past its declared maximum or past the page-table width (failed checks "
+                       "0x%x)", where, f.a, f.v, f.b, f.bits);
+    case msgl::kDebugQOffsets:
+      return MSGL_FAIL(MSGL_ERR_INDEX, "%s: request %d: q_offsets[r] = %lld and q_offsets[r+1] - "
+                       "q_offsets[r] = %d, not extend_len (failed checks 0x%x)", where, f.a, f.v,
+                       f.b, f.bits);
+    case msgl::kDebugRow:
+      return MSGL_FAIL(MSGL_ERR_INDEX, "%s: request %d: req_rows entry %lld is negative (failed "
+                       "checks 0x%x)", where, f.a, f.v, f.bits);
+    case msgl::kDebugSlot:
+      return MSGL_FAIL(MSGL_ERR_INDEX, "%s: request %d: the page-table entry read for key %d is "
+                       "%lld and reaches outside the pool (failed checks 0x%x)", where, f.a, f.b,
+                       f.v, f.bits);
+    default:
+      return MSGL_FAIL(MSGL_ERR_INDEX, "%s: request %d: out_loc = %lld is not the slot of its "
+                       "newest key %d (failed checks 0x%x)", where, f.a, f.v, f.b, f.bits);
+  }
+}
+
+int debug_gate_out_loc(const void* out_loc, bool i64, int64_t n, int64_t num_slots,
+                       hipStream_t s, const char* where) {
+  if (msgl::debug_stream_capturing(s)) return MSGL_OK;   // nothing may wait inside a capture
+  const hipError_t e = msgl::debug_check_out_loc(out_loc, i64, n, num_slots, s);
+  if (e != hipSuccess) return launch_status(e, where);
+  return debug_verdict(s, where);
+}
+
+int debug_gate_requests(const msgl::DebugRequestCheck& c, const void* store_loc, bool i64,
+                        hipStream_t s, const char* where) {
+  if (msgl::debug_stream_capturing(s)) return MSGL_OK;
+  hipError_t e = store_loc ? msgl::debug_check_out_loc(store_loc, i64, c.batch, c.num_slots, s)
+                           : hipSuccess;
+  if (e == hipSuccess) e = msgl::debug_check_requests(c, s);
+  if (e != hipSuccess) return launch_status(e, where);
+  return debug_verdict(s, where);
+}
+
+int32_t page_span(int32_t page_size) {
+  return (page_size > 1 && (page_size & (page_size - 1)) == 0) ? page_size : 1;
+}
+#endif
+
 // Compute units of the current device (cached per device).
 int device_compute_units() {
   static int cu_cache[64] = {0};
@@ -131,6 +190,14 @@ extern "C" {
 
 int msgl_version(void) { return 100; }
 
+int msgl_debug_checks(void) {
+#ifdef MSGL_DEBUG_CHECKS
+  return 1;
+#else
+  return 0;
+#endif
+}
+
 const char* msgl_status_string(int status) {
   switch (status) {
     case MSGL_OK: return "MSGL_OK";
@@ -140,6 +207,7 @@ const char* msgl_status_string(int status) {
     case MSGL_ERR_ALIGN: return "MSGL_ERR_ALIGN: pointer or stride breaks required alignment";
     case MSGL_ERR_WORKSPACE: return "MSGL_ERR_WORKSPACE: workspace missing or too small";
     case MSGL_ERR_LAUNCH: return "MSGL_ERR_LAUNCH: the HIP runtime rejected a launch";
+    case MSGL_ERR_INDEX: return "MSGL_ERR_INDEX: a device index or length is out of range (debug-check build)";
     default: return "unknown msgl status";
   }
 }
@@ -195,6 +263,10 @@ int msgl_store_kv(void* k_cache, void* v_cache, int64_t num_slots, int64_t cache
   }
   a.unit_bytes = unit;
   if (g_validate_only) return MSGL_OK;
+#ifdef MSGL_DEBUG_CHECKS
+  if (int dst = debug_gate_out_loc(out_loc, a.index_is_i64, n, num_slots, stream, "store_kv"))
+    return dst;
+#endif
   return launch_status(msgl::launch_store_kv(a), "store_kv");
 }
 
@@ -307,6 +379,22 @@ int paged_decode_impl(void* out, float* lse_out, const void* q, int64_t q_row_st
   a.meta = ws.meta_bytes ? (int32_t*)((char*)workspace + ws.part_out_bytes + ws.part_lse_bytes)
                          : nullptr;
   if (g_validate_only) return MSGL_OK;
+#ifdef MSGL_DEBUG_CHECKS
+  {
+    msgl::DebugRequestCheck c;
+    c.lens = seq_lens;
+    c.req_rows = req_rows;
+    c.pt = page_table;
+    c.pt_stride = page_table_stride;
+    c.batch = batch;
+    c.max_total = max_seq_len;
+    c.num_slots = num_slots;
+    c.page_span = page_span(page_size);
+    c.out_loc = fs ? fs->out_loc : nullptr;
+    c.out_loc_i64 = a.out_loc_is_i64;
+    if (int dst = debug_gate_requests(c, c.out_loc, a.out_loc_is_i64, stream, where)) return dst;
+  }
+#endif
   if (split_tokens > 0) {
     a.balanced_blocks = 0;
     a.max_splits = need ? (int32_t)(((int64_t)max_seq_len + split_tokens - 1) / split_tokens) : 1;
@@ -513,6 +601,23 @@ int msgl_paged_extend(void* out, float* lse_out, const void* q, int64_t q_row_st
   a.workspace_bytes = workspace_bytes;
   a.stream = stream;
   if (g_validate_only) return MSGL_OK;
+#ifdef MSGL_DEBUG_CHECKS
+  {
+    msgl::DebugRequestCheck c;
+    c.lens = prefix_lens;
+    c.ext = extend_lens;
+    c.q_offsets = q_offsets;
+    c.req_rows = req_rows;
+    c.pt = page_table;
+    c.pt_stride = page_table_stride;
+    c.batch = batch;
+    c.max_total = max_kv_len;
+    c.max_ext = max_extend_len;
+    c.num_slots = num_slots;
+    c.page_span = page_span(page_size);
+    if (int dst = debug_gate_requests(c, nullptr, false, stream, "paged_extend")) return dst;
+  }
+#endif
   return launch_status(msgl::launch_paged_extend(a), "paged_extend");
 }
 
@@ -636,6 +741,11 @@ int msgl_qk_norm_rope_store(void* q_out, int64_t q_out_row_stride, void* k_cache
   a.num_q_heads = num_q_heads;
   a.num_kv_heads = num_kv_heads;
   a.stream = stream;
+#ifdef MSGL_DEBUG_CHECKS
+  if (int dst = debug_gate_out_loc(out_loc, a.index_is_i64, n, num_slots, stream,
+                                   "qk_norm_rope_store"))
+    return dst;
+#endif
   return launch_status(msgl::launch_qk_norm_rope_store(a), "qk_norm_rope_store");
 }
 

@@ -167,4 +167,47 @@ hipError_t launch_paged_decode(const DecodeArgs& a);
 hipError_t launch_paged_extend(const ExtendArgs& a);
 hipError_t launch_merge(const MergeArgs& a);
 
+// Debug-check build (MSGL_DEBUG_CHECKS): device-side checks of the index
+// arrays, run on the call's stream before its kernels (debug_checks.hip).
+enum : unsigned int {
+  kDebugOutLoc = 1u,       // out_loc entry outside [0, num_slots)
+  kDebugLength = 2u,       // length negative, past its declared maximum or the table width
+  kDebugQOffsets = 4u,     // q_offsets[r] negative or q_offsets[r+1] - q_offsets[r] != extend_len
+  kDebugRow = 8u,          // req_rows entry negative
+  kDebugSlot = 16u,        // page-table entry read by the call outside the pool
+  kDebugNewestSlot = 32u,  // fused store: out_loc[r] is not the slot of request r's newest key
+};
+
+struct DebugRequestCheck {
+  const int32_t* lens = nullptr;       // seq_lens (decode) or prefix_lens (extend)
+  const int32_t* ext = nullptr;        // extend_lens, or null for decode
+  const int32_t* q_offsets = nullptr;  // [batch + 1], or null
+  const int32_t* req_rows = nullptr;   // or null (request r reads row r)
+  const int32_t* pt = nullptr;
+  int64_t pt_stride = 0;
+  int32_t batch = 0;
+  int32_t max_total = 0;               // max_seq_len, or max_kv_len for extend
+  int32_t max_ext = 0;                 // max_extend_len (extend)
+  int64_t num_slots = 0;
+  int32_t page_span = 1;               // P for a power-of-two page_size P > 1, else 1
+  const void* out_loc = nullptr;       // fused store + decode: new rows' slots, or null
+  int32_t out_loc_i64 = 0;
+  unsigned int* w = nullptr;           // set by debug_check_requests
+};
+
+struct DebugFailure {
+  unsigned int bits = 0;   // every failed check
+  unsigned int first = 0;  // the check of the first failure, and its details:
+  int a = 0;               // index / request
+  int b = 0;               // key, extend_len or offset step
+  long long v = 0;         // offending value
+};
+
+bool debug_stream_capturing(hipStream_t s);
+hipError_t debug_check_out_loc(const void* out_loc, bool i64, int64_t n, int64_t num_slots,
+                               hipStream_t s);
+hipError_t debug_check_requests(DebugRequestCheck c, hipStream_t s);
+// Waits for the stream, reads this device's report into *f and clears it.
+hipError_t debug_collect(hipStream_t s, DebugFailure* f);
+
 }  // namespace msgl

@@ -17,7 +17,7 @@ from paged_kv_attention_30_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "msgl.h")
 
-OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH = 0, -1, -2, -3, -4, -5, -6
+OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH, INDEX = 0, -1, -2, -3, -4, -5, -6, -7
 FAKE = 0x10000          # 64 KiB-aligned fake device address, never touched
 FAKE2 = 0x20000
 
@@ -52,9 +52,26 @@ def test_every_kvcache_symbol_is_exported(lib):
 
 def test_status_strings_and_version(lib):
     assert lib.msgl_version() >= 100
-    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH):
+    for code in (OK, NULL, SHAPE, UNSUP, ALIGN, WS, LAUNCH, INDEX):
         assert lib.msgl_status_string(code)
+    assert b"debug-check" in lib.msgl_status_string(INDEX)
     assert b"unknown" in lib.msgl_status_string(-99)
+
+
+def test_release_and_debug_check_builds():
+    """The release library trusts device indices; the debug-check build of the
+    same sources reports itself and validates host arguments the same way."""
+    import ctypes as ct
+    rel = msgl.load()
+    assert rel.msgl_debug_checks() == 0
+    dbg = ct.CDLL(binding.DEBUG_LIB_PATH)
+    dbg.msgl_debug_checks.restype = ct.c_int
+    assert dbg.msgl_debug_checks() == 1
+    with binding.using_library(binding.DEBUG_LIB_PATH) as lib:
+        assert lib.msgl_debug_checks() == 1
+        assert extend(lib, causal=0) == UNSUP
+        assert decode(lib, k=None) == NULL
+    assert msgl.load().msgl_debug_checks() == 0
 
 
 def decode(lib, **kw):
