@@ -184,3 +184,26 @@ def test_prologue_with_an_out_of_pool_slot_is_refused(dbg):
                        "out_loc[11]")
     torch.cuda.synchronize()
     assert np.array_equal(bits(kp), before[0]) and np.array_equal(bits(vp), before[1])
+
+
+def test_full_mixed_batch_at_page_size_16_passes_the_checks(dbg):
+    """The 127-request decode and the 6,144 + 2,048 extend at page_size 16
+    (the mixed benchmark batch): every check passes and the results equal
+    the release library's bit for bit."""
+    from workloads import make_config
+    banner("C5b through the debug-check library")
+    inp = make_config("C5b")
+    outs = []
+    for path in (binding.DEBUG_LIB_PATH, binding.LIB_PATH):
+        with binding.using_library(path):
+            u = Uploaded(inp)
+            u.store()
+            od, ld = u.decode()
+            oe, le = u.extend()
+            torch.cuda.synchronize()
+            outs.append((bits(od), ld.cpu().numpy().view(np.uint32), bits(oe),
+                         le.cpu().numpy().view(np.uint32)))
+            del u
+            torch.cuda.empty_cache()
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b)
