@@ -471,7 +471,8 @@ def cpu_baselines() -> dict:
     _CPU_JOB.clear()
     res["C3_extend"] = {"query_rows": len(rows), "causal_pairs": pairs, "flops": flops,
                         "one_core_s": round(t1, 4), "one_core_TFLOPs": round(flops / t1 / 1e12, 6),
-                        "all_cores_s": round(tn, 4), "all_cores_TFLOPs": round(flops / tn / 1e12, 6)}
+                        "all_cores_s": round(tn, 4), "all_cores_TFLOPs": round(flops / tn / 1e12, 6),
+                        "tokens_per_s_all_cores": round(len(rows) / tn, 1)}
     c2 = res["C2"]
     return {"value": c2["all_cores_GBps"], "unit": "GB/s", "cores": workers, "kind": "oracle",
             "sample": (f"fp64 numpy oracle, whole 64-request headline decode batch "
@@ -706,6 +707,10 @@ def summarize(name, inp, run, res, steps):
     d = {"workload": WORKLOAD_TEXT.get(name, name)}
     step_ms = res["total_ms"] / steps
     d["ms_per_step"] = round(step_ms, 4)
+    if inp.num_decode and inp.num_extend:
+        # the mixed batch's tokens per second over the whole step (decode requests
+        # plus extend tokens, store included)
+        d["step_tokens_per_s"] = round((inp.num_decode + inp.ext_tokens) / (step_ms * 1e-3), 1)
     n_new = int(inp.out_loc.shape[0])
     store_bytes = store_bytes_of(inp)
     d["store_rows"] = n_new
@@ -871,6 +876,9 @@ def main(argv=None) -> int:
         "cpu_baseline": cpu,
         "extras": extras,
         "kernel_hash": khash,
+        "peaks": {"hbm_GBps": HBM_PEAK_GBS, "mfma_bf16_dense_TFLOPs": MFMA_BF16_PEAK_TFLOPS,
+                  "clock_GHz": 2.4, "source": "MI355X published figures (the bf16 figure is "
+                  "dense, at the 2.4 GHz peak engine clock)"},
     }
     print(json.dumps(line), flush=True)
     return 0
