@@ -626,3 +626,41 @@ def test_extend_prefix_past_1024_key_tiles():
     t = torch.tensor(rows, device="cuda")
     assert_close(op[t], ro[rows], "extend 66K prefix")
     assert_lse_close(lp[t], rl[rows], "extend 66K prefix lse")
+
+
+@pytest.mark.parametrize("P", [2, 8, 64, 256, 3])
+def test_other_page_sizes_match_page_size_1(P):
+    """Page sizes other than 16 on a table of P-slot pages (page permutation):
+    decode (balanced and 96-key chunks) and extend bit-identical to
+    page_size 1 on the same table, and held to the oracle.  For a power of
+    two every non-first column of each page is overwritten by out-of-pool
+    values first, so only page starts may be read; P = 3 (not a power of two)
+    reads every column, so its table stays intact."""
+    banner(f"page_size {P} vs 1")
+    inp = small_extend(160 + P, 32, 8, [(3 * P + 5, 70), (0, 50)], page_size=P,
+                       num_slots=max(16384, 64 * P), decode_lens=[700, 1, 2 * P + 1, 130])
+    u = Uploaded(inp)
+    u.store()
+    d1, dl1 = u.decode(page_size=1)
+    f1, fl1 = u.decode(page_size=1, split_tokens=96)
+    e1, el1 = u.extend(page_size=1)
+    if P & (P - 1) == 0:
+        poisoned = inp.page_table.copy()
+        cols = np.arange(poisoned.shape[1]) % P != 0
+        poisoned[:, cols] = inp.num_slots + 7 + np.arange(int(cols.sum()), dtype=np.int32)
+        u.pt = up(poisoned)
+    dp, dlp = u.decode(page_size=P)
+    fp, flp = u.decode(page_size=P, split_tokens=96)
+    ep, elp = u.extend(page_size=P)
+    torch.cuda.synchronize()
+    for a, b, what in ((dp, d1, "decode"), (fp, f1, "decode 96-key chunks"), (ep, e1, "extend")):
+        assert np.array_equal(bits(a), bits(b)), what
+    for a, b, what in ((dlp, dl1, "decode lse"), (flp, fl1, "chunked lse"), (elp, el1, "extend lse")):
+        assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32)), what
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle_decode(inp, kp, vp)
+    assert_close(dp, ro, f"decode page_size {P}")
+    assert_lse_close(dlp, rl, f"decode page_size {P} lse")
+    re, rel = oracle_extend(inp, kp, vp)
+    assert_close(ep, re, f"extend page_size {P}")
+    assert_lse_close(elp, rel, f"extend page_size {P} lse")
