@@ -117,6 +117,13 @@ DECODE_CASES = [
     (16, 1, [300, 45], 32),
     (32, 2, [90, 1000, 1001], 128),
     (4, 2, [5, 40], 0),
+    # more kv heads than one workgroup takes (16 and 32: two and four groups
+    # of 8), and 4 kv heads
+    (16, 16, [700, 1, 129, 2000], 0),
+    (16, 16, [700, 1, 129, 2000], 128),
+    (32, 32, [300, 1025, 64], 0),
+    (8, 4, [1, 500, 33], 0),
+    (64, 4, [1200, 7], 64),
 ]
 
 
@@ -345,6 +352,10 @@ EXTEND_CASES = [
     (16, 8, [(0, 257), (1, 3)]),
     (64, 8, [(200, 40), (0, 77)]),
     (16, 1, [(90, 70)]),
+    (16, 16, [(100, 90), (0, 40)]),
+    (32, 32, [(64, 70)]),
+    (8, 4, [(33, 129)]),
+    (32, 2, [(5, 100), (0, 17)]),
 ]
 
 
