@@ -70,6 +70,11 @@ CASES = [
     # GQA ratio 8 in balanced mode (the long-tail batch's launch), lengths
     # past 4K keys so requests are cut across workgroups
     (64, 8, [5000, 1024, 7, 2048, 4711, 1300, 64, 3333], 0, 1, np.int64),
+    # kv heads spread over two and four workgroups: each stores its own heads'
+    # slices of the new rows
+    (16, 16, [700, 1, 129, 2000, 33], 0, 1, np.int32),
+    (32, 32, [300, 1025, 64], 0, 1, np.int64),
+    (16, 16, [700, 1, 129, 2000, 33], 128, 1, np.int32),
 ]
 
 
