@@ -675,3 +675,47 @@ def test_other_page_sizes_match_page_size_1(P):
     re, rel = oracle_extend(inp, kp, vp)
     assert_close(ep, re, f"extend page_size {P}")
     assert_lse_close(elp, rel, f"extend page_size {P} lse")
+
+
+def test_extend_q_from_a_merged_qkv_buffer_and_no_lse():
+    """q as the attention layer hands it over after the prologue: the first
+    Hq * 128 columns of a merged [T, (Hq + 2 Hkv) * 128] qkv buffer (row stride
+    (Hq + 2 Hkv) * 128); the same call without an lse output.  Outputs equal
+    the contiguous-q call bitwise."""
+    banner("extend q strided in qkv, no lse")
+    hq, hkv = 32, 8
+    inp = small_extend(170, hq, hkv, [(40, 90), (0, 33)], num_slots=4096)
+    u = Uploaded(inp)
+    u.store()
+    ref, ref_lse = u.extend()
+    T = inp.ext_q.shape[0]
+    qkv = torch.zeros((T, (hq + 2 * hkv) * 128), dtype=torch.bfloat16, device="cuda")
+    qkv[:, :hq * 128] = u.eq.reshape(T, hq * 128)
+    q = qkv[:, :hq * 128].view(T, hq, 128)
+    assert q.stride(0) == (hq + 2 * hkv) * 128
+    out, lse = msgl.paged_extend(q, u.k, u.v, u.pt, u.e_pre, u.e_ext, u.e_off, u.e_max, u.e_kv,
+                                 inp.sm_scale, req_rows=u.e_rows)
+    out2, lse2 = msgl.paged_extend(q, u.k, u.v, u.pt, u.e_pre, u.e_ext, u.e_off, u.e_max, u.e_kv,
+                                   inp.sm_scale, req_rows=u.e_rows, want_lse=False)
+    torch.cuda.synchronize()
+    assert lse2 is None
+    assert np.array_equal(bits(out), bits(ref)) and np.array_equal(bits(out2), bits(ref))
+    assert np.array_equal(lse.cpu().numpy().view(np.uint32), ref_lse.cpu().numpy().view(np.uint32))
+    kp, vp = oracle_pool(inp)
+    ro, _ = oracle_extend(inp, kp, vp)
+    assert_close(out, ro, "extend strided q")
+
+
+@pytest.mark.parametrize("split", [0, 64])
+def test_decode_without_lse_output(split):
+    """No lse output (lse_out NULL): outputs equal the call that writes it,
+    with requests finished in one workgroup and requests merged from parts."""
+    banner(f"decode no lse split={split}")
+    inp = small_decode(171, 32, 8, [3000, 5, 700, 64], num_slots=8192)
+    u = Uploaded(inp)
+    u.store()
+    ref, _ = u.decode(split_tokens=split)
+    out, lse = u.decode(split_tokens=split, want_lse=False)
+    torch.cuda.synchronize()
+    assert lse is None
+    assert np.array_equal(bits(out), bits(ref))
