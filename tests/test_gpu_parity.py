@@ -719,3 +719,20 @@ def test_decode_without_lse_output(split):
     torch.cuda.synchronize()
     assert lse is None
     assert np.array_equal(bits(out), bits(ref))
+
+
+def test_extend_is_deterministic():
+    """Three planned runs of a batch whose planner orders items with LDS
+    atomics (so the dispatch order may differ run to run): bitwise equal."""
+    banner("extend determinism")
+    inp = small_extend(172, 32, 8, [(900, 300), (0, 257), (2048, 64), (100, 100), (5, 700)],
+                       num_slots=8192)
+    u = Uploaded(inp)
+    u.store()
+    outs = []
+    for _ in range(3):
+        o, l = u.extend()
+        torch.cuda.synchronize()
+        outs.append((bits(o), l.cpu().numpy().view(np.uint32)))
+    for o, l in outs[1:]:
+        assert np.array_equal(o, outs[0][0]) and np.array_equal(l, outs[0][1])
