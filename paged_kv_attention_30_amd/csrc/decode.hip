@@ -18,10 +18,12 @@
 //   of §4.6.4; P = 1 (or any other P) reads every column.  Slots are clamped
 //   to the pool, so a bad entry cannot address memory outside it.
 // * Work split ("balanced" mode, split_tokens = 0): the keys of the whole
-//   batch, laid end to end in request order, are cut into gridDim.x equal
-//   ranges, one per workgroup; the grid is sized to the number of
-//   workgroups the GPU holds at once, so the whole batch runs in a single
-//   round with equal work everywhere.  A range may cover the tail of one
+//   batch, laid end to end in request order with a fixed start-up cost
+//   (kSegmentCost) in front of each request's keys, are cut into ranges of
+//   equal cost, one per workgroup; each working workgroup's range costs at
+//   least kMinKeysPerBlock, so a small batch uses fewer workgroups.
+//   The grid is at most the number of workgroups the GPU holds at once, so
+//   the whole batch runs in a single round.  A range may cover the tail of one
 //   request, several whole requests and the head of another; a request
 //   covered by one workgroup is finished there, a request cut across
 //   workgroups leaves normalised fp32 partials + lse that the merge kernel
