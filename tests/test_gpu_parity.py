@@ -677,6 +677,53 @@ def test_other_page_sizes_match_page_size_1(P):
     assert_lse_close(elp, rel, f"extend page_size {P} lse")
 
 
+@pytest.mark.parametrize("hq,hkv", [(4, 1), (8, 2), (8, 1)])
+def test_tensor_parallel_shard_shapes_at_page_size_16(hq, hkv):
+    """One tensor-parallel rank's share of the heads (one or two kv heads) on a
+    table of 16-slot pages: balanced decode with requests cut across
+    workgroups, the same decode with the new rows stored in the launch, and
+    extend.  Every non-first column of each page is overwritten with
+    out-of-pool values, so only page starts may be read.  Results are
+    bit-identical to page_size 1 on the intact table and held to the oracle."""
+    banner(f"shard hq={hq} hkv={hkv} page_size 16")
+    P = 16
+    inp = small_extend(190 + hq + hkv, hq, hkv, [(3 * P + 5, 70), (0, 50)], page_size=P,
+                       num_slots=16384, decode_lens=[3000, 17, 900, 1, 2500])
+    B = inp.num_decode
+    u = Uploaded(inp)
+    u.store()
+    loc = up(inp.out_loc[-B:].astype(np.int32))
+
+    def fused(ps):
+        return msgl.store_kv_paged_decode(u.dq, u.k, u.v, u.k_new[-B:], u.v_new[-B:], loc, u.pt,
+                                          u.d_lens, u.d_max, inp.sm_scale, req_rows=u.d_rows,
+                                          page_size=ps)
+
+    d1, dl1 = u.decode(page_size=1)
+    f1, fl1 = fused(1)
+    e1, el1 = u.extend(page_size=1)
+    poisoned = inp.page_table.copy()
+    cols = np.arange(poisoned.shape[1]) % P != 0
+    poisoned[:, cols] = inp.num_slots + 7 + np.arange(int(cols.sum()), dtype=np.int32)
+    u.pt = up(poisoned)
+    dp, dlp = u.decode(page_size=P)
+    fp, flp = fused(P)
+    ep, elp = u.extend(page_size=P)
+    torch.cuda.synchronize()
+    for a, b, what in ((dp, d1, "decode"), (fp, f1, "fused store + decode"), (ep, e1, "extend")):
+        assert np.array_equal(bits(a), bits(b)), what
+    for a, b, what in ((dlp, dl1, "decode lse"), (flp, fl1, "fused lse"), (elp, el1, "extend lse")):
+        assert np.array_equal(a.cpu().numpy().view(np.uint32), b.cpu().numpy().view(np.uint32)), what
+    assert np.array_equal(bits(fp), bits(dp)), "fused vs two-call"
+    kp, vp = oracle_pool(inp)
+    ro, rl = oracle_decode(inp, kp, vp)
+    assert_close(dp, ro, f"shard decode hq={hq} hkv={hkv}")
+    assert_lse_close(dlp, rl, f"shard decode lse hq={hq} hkv={hkv}")
+    re, rel = oracle_extend(inp, kp, vp)
+    assert_close(ep, re, f"shard extend hq={hq} hkv={hkv}")
+    assert_lse_close(elp, rel, f"shard extend lse hq={hq} hkv={hkv}")
+
+
 def test_extend_q_from_a_merged_qkv_buffer_and_no_lse():
     """q as the attention layer hands it over after the prologue: the first
     Hq * 128 columns of a merged [T, (Hq + 2 Hkv) * 128] qkv buffer (row stride
