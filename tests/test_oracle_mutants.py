@@ -15,7 +15,7 @@ import numpy as np
 import pytest
 
 from workloads import small_decode, small_extend
-from tests.brute import decode_brute, sdpa_extend
+from tests.brute import brute_attention, bits_to_float, decode_brute, sdpa_extend
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(__file__)), "oracle", "attention.py")
 
@@ -55,6 +55,33 @@ def check_extend_sdpa(orc) -> bool:
     return bool(ok)
 
 
+def check_extend_lse_brute(orc) -> bool:
+    """Every extend row's lse against the pure-Python brute force over its
+    visible keys (prefix plus the new tokens up to its own)."""
+    inp = small_extend(34, 4, 2, [(3, 4), (0, 3)], head_dim=8, num_slots=64)
+    k, v = orc.store_kv(inp.k_pool, inp.v_pool, inp.k_new, inp.v_new, inp.out_loc)
+    _, lse = orc.paged_extend(inp.ext_q, k, v, inp.page_table, inp.ext_req_rows,
+                              inp.ext_prefix_lens, inp.ext_extend_lens, inp.ext_q_offsets,
+                              inp.sm_scale, 2)
+    Hq = inp.ext_q.shape[1]
+    ratio = Hq // 2
+    for r in range(len(inp.ext_prefix_lens)):
+        row = int(inp.ext_req_rows[r])
+        P, E, base = (int(inp.ext_prefix_lens[r]), int(inp.ext_extend_lens[r]),
+                      int(inp.ext_q_offsets[r]))
+        for ii in range(E):
+            slots = [int(inp.page_table[row, j]) for j in range(P + ii + 1)]
+            for h in range(Hq):
+                g = h // ratio
+                qv = [bits_to_float(x) for x in inp.ext_q[base + ii, h]]
+                ks = [[bits_to_float(x) for x in k[sl, g]] for sl in slots]
+                vs = [[bits_to_float(x) for x in v[sl, g]] for sl in slots]
+                _, lb = brute_attention(qv, ks, vs, inp.sm_scale)
+                if abs(lse[base + ii, h] - lb) > 1e-10:
+                    return False
+    return True
+
+
 def check_split_merge(orc) -> bool:
     inp = small_decode(33, 4, 2, [50, 17, 3], num_slots=256)
     o, l = orc.paged_decode(inp.dec_q, inp.k_pool, inp.v_pool, inp.page_table,
@@ -80,7 +107,7 @@ def check_store(orc) -> bool:
         vo.reshape(-1).tolist() == [100, 101, 810, 811, 104, 105, 800, 801]
 
 
-ALL_CHECKS = [check_decode_brute, check_extend_sdpa, check_split_merge,
+ALL_CHECKS = [check_decode_brute, check_extend_sdpa, check_extend_lse_brute, check_split_merge,
               check_merge_closed_form, check_store]
 
 MUTANTS = {
@@ -99,6 +126,14 @@ MUTANTS = {
                                      "vals = gather_rows(k_pool, page_table[row], b, e, g)"),
     "extend reads q of the wrong request": ("s = sm_scale * (qf[base + ii, h, :] @ keys.T)",
                                             "s = sm_scale * (qf[ii, h, :] @ keys.T)"),
+    "decode output not normalised": ("out = (p @ values) / denom", "out = (p @ values)"),
+    "extend output not normalised": ("out[base + ii, h, :] = (p @ vals) / denom",
+                                     "out[base + ii, h, :] = (p @ vals)"),
+    "decode lse in base 2": ("lse = m + math.log(denom)", "lse = m + math.log2(denom)"),
+    "extend lse in base 2": ("lse[base + ii, h] = m[:, 0] + np.log(denom[:, 0])",
+                             "lse[base + ii, h] = m[:, 0] + np.log2(denom[:, 0])"),
+    "split chunks drop their last key": ("e = [min((c + 1) * split_tokens, x) for x in L]",
+                                         "e = [min((c + 1) * split_tokens - 1, x) for x in L]"),
 }
 
 
